@@ -1,0 +1,247 @@
+"""Python binding of libfp8mi.so, the MI355X (gfx950) FP8 scaled-quantization
+and scaled-FP8-GEMM library.
+
+The three entry points keep the C names and arguments of include/fp8mi.h
+(``fp8_quantize``, ``fp8_amax_history_update``, ``fp8_gemm_scaled``); this
+module only marshals torch tensors into device pointers and passes torch's
+current HIP stream.  Every step of the computation runs in the library's
+kernels.  ``quantize`` / ``gemm`` / ``DelayedState`` below allocate the output
+tensors with torch and call those same entry points.
+
+Importing this module does not load the library; the first call does, and
+raises if it has not been built (``python -m fp8_scaled_quantization_scale_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8mi.so")
+
+# values of the FP8MI_* macros in include/fp8mi.h
+OK = 0
+ERR_NULL, ERR_ENUM, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP = -1, -2, -3, -4, -5, -6
+E4M3, E5M2 = 0, 1
+IN_BF16, IN_FP32 = 0, 1
+OUT_BF16, OUT_FP32 = 0, 1
+TENSOR_CURRENT, TENSOR_DELAYED, BLOCK_1x128, BLOCK_128x128, MX_1x32 = 0, 1, 2, 3, 4
+ROW, COL, ROW_AND_COL = 1, 2, 3
+GEMM_TENSOR, GEMM_BLOCK_1x128_128x128, GEMM_BLOCK_1x128_1x128, GEMM_MX_1x32 = 0, 1, 2, 3
+
+FMT = {"e4m3": E4M3, "e5m2": E5M2}
+TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+
+EXPORTS = ("fp8_quantize", "fp8_amax_history_update", "fp8_gemm_scaled",
+           "fp8_status_string", "fp8_version")
+
+
+class Fp8Error(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libfp8mi.so (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise Fp8Error(f"{path} not built; run python -m fp8_scaled_quantization_scale_amd.build")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.fp8_quantize.restype = i32
+    lib.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, i32,
+                                 vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp]
+    lib.fp8_amax_history_update.restype = i32
+    lib.fp8_amax_history_update.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp, vp, vp]
+    lib.fp8_gemm_scaled.restype = i32
+    lib.fp8_gemm_scaled.argtypes = [vp, i32, vp, i64, vp, i32, vp, i64, i32, i64, i64, i64,
+                                    vp, i32, i64, vp]
+    lib.fp8_status_string.restype = ctypes.c_char_p
+    lib.fp8_status_string.argtypes = [i32]
+    lib.fp8_version.restype = i32
+    lib.fp8_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _p(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        msg = load().fp8_status_string(status).decode()
+        raise Fp8Error(f"{what} failed ({status}): {msg}")
+
+
+def status_string(status: int) -> str:
+    return load().fp8_status_string(status).decode()
+
+
+def version() -> int:
+    return load().fp8_version()
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, argument for argument (tensors or raw pointers)
+# ---------------------------------------------------------------------------
+
+def fp8_quantize(x, x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin,
+                 q_row, ld_q_row, s_row, q_col, ld_q_col, s_col,
+                 scale, scale_inv, amax, nonfinite, stream=None) -> int:
+    return load().fp8_quantize(_p(x), x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin,
+                               _p(q_row), ld_q_row, _p(s_row), _p(q_col), ld_q_col, _p(s_col),
+                               _p(scale), _p(scale_inv), _p(amax), _p(nonfinite), _stream(stream))
+
+
+def fp8_amax_history_update(history, head, length, amax, fmt, margin, scale, scale_inv,
+                            nonfinite, stream=None) -> int:
+    return load().fp8_amax_history_update(_p(history), _p(head), length, _p(amax), fmt, margin,
+                                          _p(scale), _p(scale_inv), _p(nonfinite), _stream(stream))
+
+
+def fp8_gemm_scaled(a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, M, N, K, c, c_dtype, ldc,
+                    stream=None) -> int:
+    return load().fp8_gemm_scaled(_p(a), fmt_a, _p(s_a), lda, _p(b), fmt_b, _p(s_b), ldb, recipe,
+                                  M, N, K, _p(c), c_dtype, ldc, _stream(stream))
+
+
+# ---------------------------------------------------------------------------
+# conveniences: allocate outputs with torch, call the entry points above
+# ---------------------------------------------------------------------------
+
+def _ceil(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+def _pad16(n: int) -> int:
+    return _ceil(max(n, 1), 16) * 16
+
+
+@dataclass
+class Quantized:
+    """Codes (uint8) and scales of one fp8_quantize call."""
+    fmt: int
+    recipe: int
+    q_row: torch.Tensor | None = None   # [rows x ld_q_row] codes, first `cols` columns used
+    s_row: torch.Tensor | None = None
+    q_col: torch.Tensor | None = None   # [cols x ld_q_col] codes of x^T
+    s_col: torch.Tensor | None = None
+    scale: torch.Tensor | None = None
+    scale_inv: torch.Tensor | None = None
+    amax: torch.Tensor | None = None
+    nonfinite: torch.Tensor | None = None
+
+
+def scale_grid_shape(recipe: int, rows: int, cols: int, orient: int):
+    """Shape and dtype of the ROW (orient=ROW) or COL scale grid of fp8_quantize."""
+    if recipe == BLOCK_1x128:
+        return ((rows, _ceil(cols, 128)) if orient == ROW else (cols, _ceil(rows, 128))), torch.float32
+    if recipe == BLOCK_128x128:
+        g = (_ceil(rows, 128), _ceil(cols, 128))
+        return (g if orient == ROW else (g[1], g[0])), torch.float32
+    if recipe == MX_1x32:
+        return ((rows, _ceil(cols, 32)) if orient == ROW else (cols, _ceil(rows, 32))), torch.uint8
+    return None, None
+
+
+def quantize(x: torch.Tensor, recipe: int, fmt: int, orient: int = ROW, margin: int = 0,
+             scale: torch.Tensor | None = None, amax: torch.Tensor | None = None,
+             nonfinite: torch.Tensor | None = None, stream=None) -> Quantized:
+    """Quantize a 2-D BF16/FP32 device tensor (row-major, ld = its stride)."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    dev = x.device
+    x_dtype = IN_BF16 if x.dtype == torch.bfloat16 else IN_FP32
+    out = Quantized(fmt=fmt, recipe=recipe)
+    ld_r = _pad16(cols)
+    ld_c = _pad16(rows)
+    if orient & ROW:
+        out.q_row = torch.empty(rows, ld_r, dtype=torch.uint8, device=dev)
+        shp, dt = scale_grid_shape(recipe, rows, cols, ROW)
+        if shp is not None:
+            out.s_row = torch.empty(shp, dtype=dt, device=dev)
+    if orient & COL:
+        out.q_col = torch.empty(cols, ld_c, dtype=torch.uint8, device=dev)
+        shp, dt = scale_grid_shape(recipe, rows, cols, COL)
+        if shp is not None:
+            out.s_col = torch.empty(shp, dtype=dt, device=dev)
+    if recipe in (TENSOR_CURRENT, TENSOR_DELAYED):
+        out.scale = scale if scale is not None else torch.ones(1, dtype=torch.float32, device=dev)
+        if recipe == TENSOR_CURRENT:  # delayed leaves scale_inv to the history update
+            out.scale_inv = torch.empty(1, dtype=torch.float32, device=dev)
+        out.amax = amax if amax is not None else torch.zeros(1, dtype=torch.float32, device=dev)
+    out.nonfinite = nonfinite
+    st = fp8_quantize(x, x_dtype, rows, cols, x.stride(0), recipe, fmt, orient, margin,
+                      out.q_row, ld_r, out.s_row, out.q_col, ld_c, out.s_col,
+                      out.scale, out.scale_inv, out.amax, nonfinite, stream)
+    _check(st, "fp8_quantize")
+    return out
+
+
+def gemm(a: torch.Tensor, fmt_a: int, s_a: torch.Tensor, b: torch.Tensor, fmt_b: int,
+         s_b: torch.Tensor, recipe: int, K: int, out_dtype=torch.bfloat16,
+         M: int | None = None, N: int | None = None, c: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """C[M x N] = dequant(a[:, :K]) . dequant(b[:, :K])^T (a, b uint8 codes, row-major)."""
+    M = a.shape[0] if M is None else M
+    N = b.shape[0] if N is None else N
+    if c is None:
+        c = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    c_dtype = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_FP32
+    st = fp8_gemm_scaled(a, fmt_a, s_a, a.stride(0), b, fmt_b, s_b, b.stride(0), recipe,
+                         M, N, K, c, c_dtype, c.stride(0), stream)
+    _check(st, "fp8_gemm_scaled")
+    return c
+
+
+class DelayedState:
+    """Device-resident delayed-scaling state: amax ring, head, scale,
+    scale_inv, the amax accumulator and a non-finite counter."""
+
+    def __init__(self, fmt: int, length: int = 200, margin: int = 0, device="cuda"):
+        self.fmt, self.length, self.margin = fmt, length, margin
+        self.history = torch.zeros(length, dtype=torch.float32, device=device)
+        self.head = torch.zeros(1, dtype=torch.int32, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(1, dtype=torch.float32, device=device)
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self.nonfinite = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def quantize(self, x: torch.Tensor, orient: int = ROW, stream=None) -> Quantized:
+        q = quantize(x, TENSOR_DELAYED, self.fmt, orient, self.margin, scale=self.scale,
+                     amax=self.amax, stream=stream)
+        q.scale_inv = self.scale_inv.clone()
+        return q
+
+    def update(self, stream=None):
+        st = fp8_amax_history_update(self.history, self.head, self.length, self.amax, self.fmt,
+                                     self.margin, self.scale, self.scale_inv, self.nonfinite, stream)
+        _check(st, "fp8_amax_history_update")
+
+    def state_dict(self):
+        return {k: getattr(self, k).clone() for k in
+                ("history", "head", "scale", "scale_inv", "amax", "nonfinite")}
+
+    def load_state_dict(self, sd):
+        for k, v in sd.items():
+            getattr(self, k).copy_(v)

@@ -1,0 +1,56 @@
+// launch.hpp -- internal launchers behind the C ABI (include/fp8mi.h).
+// Arguments arrive here already validated by the host-side checks in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mi {
+
+// values mirror the FP8MI_* macros of the public header
+constexpr int kInBf16 = 0, kInFp32 = 1;
+constexpr int kOutBf16 = 0, kOutFp32 = 1;
+constexpr int kRecipeTensorCurrent = 0, kRecipeTensorDelayed = 1, kRecipeBlock1x128 = 2,
+              kRecipeBlock128x128 = 3, kRecipeMx1x32 = 4;
+constexpr int kGemmTensor = 0, kGemmBlock128x128 = 1, kGemmBlock1x128 = 2, kGemmMx = 3;
+
+struct QuantParams {
+  const void* x;
+  int x_dtype;
+  int64_t rows, cols, ld_x;
+  int recipe, fmt, orient, margin;
+  uint8_t* q_row;
+  int64_t ld_q_row;
+  void* s_row;
+  uint8_t* q_col;
+  int64_t ld_q_col;
+  void* s_col;
+  float* scale;
+  float* scale_inv;
+  float* amax;
+  int32_t* nonfinite;
+};
+
+struct GemmParams {
+  const uint8_t* a;
+  int fmt_a;
+  const void* s_a;
+  int64_t lda;
+  const uint8_t* b;
+  int fmt_b;
+  const void* s_b;
+  int64_t ldb;
+  int recipe;
+  int64_t M, N, K;
+  void* c;
+  int c_dtype;
+  int64_t ldc;
+};
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t st);
+hipError_t launch_empty_scale(float* scale, float* scale_inv, hipStream_t st);
+hipError_t launch_history(float* history, int32_t* head, int len, float* amax, int fmt, int margin,
+                          float* scale, float* scale_inv, int32_t* nonfinite, hipStream_t st);
+hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
+
+}  // namespace fp8mi

@@ -1,0 +1,194 @@
+/*
+ * fp8mi.h -- C ABI of the MI355X (gfx950) FP8 scaled-quantization and
+ * scaled-FP8-GEMM library (libfp8mi.so).
+ *
+ * What is computed (cited by page and section; the pages are web articles
+ * on FP8 training):
+ *   [P1] "2025 technical guide: FP8 quantized training" (blog.gitcode.com)
+ *        sec. 1.1  E4M3 / E5M2 bit layouts;
+ *        sec. 2.1  per-tensor scaling: delayed (amax history over the past
+ *                  steps, usually 200, scale from the history maximum) and
+ *                  current (amax of the tensor being cast);
+ *        sec. 2.2  blockwise scaling: 1x128 tiles for inputs and gradients,
+ *                  128x128 tiles for weights, one scale per tile;
+ *        sec. 2.3  MXFP8: 1x32 blocks with E8M0 power-of-two scales;
+ *        sec. 3.1  the three GEMMs (fprop, dgrad, wgrad) take quantized
+ *                  inputs and keep BF16/FP32 outputs.
+ *   [P2] "From FP16 to FP8" (bjdmk.com.cn/news/5220490) sec. 1-2: E5M2
+ *        range 57344 .. 6.1e-5, bias 15; sec. 3.3: DelayedScaling with
+ *        margin and an update every step.
+ *   [P3] "Mastering FP8 LLM training" (nmedialink.com) strategies 1-4
+ *        (delayed, current, sub-channel blocks that need re-quantization
+ *        on transpose, MXFP8) and Fig. 1 (GEMM cost by scaling granularity).
+ *   [P4] "FP8 training support" (bjdmk.com.cn/news/366077) "Why FP8?":
+ *        E4M3 for weights/activations, E5M2 for gradients; a per-tensor
+ *        scale maps the FP32 range onto the FP8 range.
+ *
+ * Numerics (identical bit for bit to the CPU oracle):
+ *   E4M3 = OCP E4M3FN (max 448, subnormals, NaN 0x7F/0xFF, no Inf);
+ *   E5M2 = OCP E5M2 (max 57344, subnormals, Inf 0x7C/0xFC).
+ *   code = enc(fl32(x * s)): one binary32 multiply, then round to nearest,
+ *   ties to the even code, saturating (|v| >= max and +-Inf give +-max),
+ *   NaN gives 0x7F, -0 gives 0x80.
+ *   s = fl32(max / amax) * 2^-margin (amax == 0 or non-finite: s = 1;
+ *   +Inf: FLT_MAX); s_inv = fl32(1 / s) is the dequantisation scale the
+ *   GEMM consumes.  MX: E8M0 byte e + 127 with e = ceil(log2(amax / max))
+ *   clamped to [-127, 127] (amax == 0: 127; non-finite: 0xFF), elements
+ *   enc(fl32(x * 2^-e)).
+ *
+ * Conventions:
+ *   - Every matrix is row-major with an explicit leading dimension counted
+ *     in elements.  Tensor and scale pointers are DEVICE pointers; `stream`
+ *     is a hipStream_t (NULL = the null stream).
+ *   - The library allocates nothing, keeps no state between calls and
+ *     never synchronises the host: all work is enqueued on `stream`.
+ *     Calls that write the same buffers on different streams race.
+ *   - Return values report host-checkable errors only.  Data-dependent
+ *     conditions (NaN/Inf inputs) are reported through device outputs:
+ *     a non-finite amax, and the `nonfinite` counters.
+ *   - Weights are stored [out x in] = [N x K], so every GEMM operand is
+ *     row-major with the contraction index contiguous ("TN" layout).
+ */
+#ifndef FP8MI_H
+#define FP8MI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define FP8MI_OK 0
+#define FP8MI_ERR_NULL (-1)        /* a required pointer is NULL            */
+#define FP8MI_ERR_ENUM (-2)        /* unknown recipe / format / dtype value */
+#define FP8MI_ERR_SHAPE (-3)       /* negative size, ld too small, margin   */
+#define FP8MI_ERR_UNSUPPORTED (-4) /* valid values, combination not built   */
+#define FP8MI_ERR_ALIGN (-5)       /* pointer or ld breaks 16-byte alignment */
+#define FP8MI_ERR_HIP (-6)         /* a HIP launch failed                   */
+
+/* ---- enums ------------------------------------------------------------ */
+#define FP8MI_E4M3 0 /* OCP E4M3FN */
+#define FP8MI_E5M2 1 /* OCP E5M2   */
+
+#define FP8MI_IN_BF16 0
+#define FP8MI_IN_FP32 1
+
+#define FP8MI_OUT_BF16 0
+#define FP8MI_OUT_FP32 1
+
+/* quantize recipes [P1 sec. 2.1-2.3] */
+#define FP8MI_TENSOR_CURRENT 0 /* amax of x now -> s; writes amax, scale, scale_inv    */
+#define FP8MI_TENSOR_DELAYED 1 /* cast with *scale; max-accumulates amax of x into *amax */
+#define FP8MI_BLOCK_1x128 2    /* ROW: 1x128 along cols; COL: 128x1 down rows            */
+#define FP8MI_BLOCK_128x128 3  /* one scale per 128x128 tile                             */
+#define FP8MI_MX_1x32 4        /* ROW: 1x32 along cols; COL: 32x1 down rows; E8M0 bytes  */
+
+/* which code layouts to write */
+#define FP8MI_ROW 1         /* q_row [rows x cols]                          */
+#define FP8MI_COL 2         /* q_col [cols x rows] = codes written transposed */
+#define FP8MI_ROW_AND_COL 3 /* both, from one read of x                      */
+
+/* GEMM scale recipes [P1 sec. 2.1-2.3, 3.1] */
+#define FP8MI_GEMM_TENSOR 0            /* s_a, s_b: one float each (scale_inv)              */
+#define FP8MI_GEMM_BLOCK_1x128_128x128 1 /* s_a [M x ceil(K/128)], s_b [ceil(N/128) x ceil(K/128)] */
+#define FP8MI_GEMM_BLOCK_1x128_1x128 2   /* s_a [M x ceil(K/128)], s_b [N x ceil(K/128)]      */
+#define FP8MI_GEMM_MX_1x32 3             /* s_a [M x ceil(K/32)], s_b [N x ceil(K/32)] E8M0   */
+
+/* ---- entry points ----------------------------------------------------- */
+
+/* fp8_quantize -- scaled cast of x [rows x cols] (BF16 or FP32) to FP8 codes.
+ * [P1 sec. 2.1 (per-tensor current / delayed), 2.2 (1x128, 128x128),
+ *  2.3 (MX 1x32 + E8M0); P3 strategy 3 (re-quantize for the transposed use)]
+ *
+ *   x, x_dtype, rows, cols, ld_x : input, ld_x >= cols elements.
+ *   recipe, fmt, orient, margin  : FP8MI_* values above; margin in [0, 64]
+ *                                  (per-tensor and FP32-scale block recipes;
+ *                                  ignored by MX).
+ *   q_row, ld_q_row, s_row       : ROW output.  Codes [rows x cols].
+ *        BLOCK_1x128   s_row = float [rows x ceil(cols/128)]   (s_inv per block)
+ *        BLOCK_128x128 s_row = float [ceil(rows/128) x ceil(cols/128)]
+ *        MX_1x32       s_row = uint8 [rows x ceil(cols/32)]    (E8M0 bytes)
+ *        TENSOR_*      s_row unused.
+ *   q_col, ld_q_col, s_col       : COL output.  Codes of x^T, [cols x rows].
+ *        BLOCK_1x128   blocks run 128 rows down each column:
+ *                      s_col = float [cols x ceil(rows/128)]
+ *        BLOCK_128x128 same tiles and scales as ROW, grid transposed:
+ *                      s_col = float [ceil(cols/128) x ceil(rows/128)]
+ *        MX_1x32       32 rows down each column:
+ *                      s_col = uint8 [cols x ceil(rows/32)]
+ *        TENSOR_*      same scale as ROW (a plain transpose of the codes).
+ *   scale, scale_inv, amax       : per-tensor recipes only (device floats).
+ *        CURRENT: writes amax = max|x| (NaN if x holds a NaN), scale and
+ *                 scale_inv.
+ *        DELAYED: reads *scale; *amax = max(*amax, max|x|) -- the caller
+ *                 zeroes it once, fp8_amax_history_update consumes and
+ *                 re-zeroes it; scale_inv is not touched.
+ *   nonfinite                    : optional (may be NULL) device int32; gets
+ *        += the number of scale blocks whose amax was NaN/Inf (CURRENT and
+ *        block recipes; those blocks use s = 1, MX byte 0xFF).
+ * Alignment: x, q_row, q_col 16-byte aligned; ld_x * sizeof(elem),
+ * ld_q_row and ld_q_col multiples of 16 bytes.  rows == 0 or cols == 0 is
+ * allowed (CURRENT then writes amax = 0, scale = scale_inv = 1).
+ * Returns FP8MI_OK or an FP8MI_ERR_* code; nothing is launched on error. */
+int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                 int recipe, int fmt, int orient, int margin,
+                 uint8_t* q_row, int64_t ld_q_row, void* s_row,
+                 uint8_t* q_col, int64_t ld_q_col, void* s_col,
+                 float* scale, float* scale_inv, float* amax, int32_t* nonfinite,
+                 void* stream);
+
+/* fp8_amax_history_update -- one delayed-scaling step.
+ * [P1 sec. 2.1: amax history over the past steps (usually 200), scale from
+ *  the maximum of the buffer; P2 sec. 3.3: interval 1 = every step, margin]
+ *
+ *   history  : float [len] ring, zero-initialised by the caller; head: int32.
+ *   amax     : float, the amax accumulated since the previous update (as
+ *              written by fp8_quantize with TENSOR_DELAYED); read, then
+ *              reset to 0.
+ *   If *amax is finite it is written to history[*head] and
+ *   head = (head + 1) % len; otherwise *nonfinite += 1 and nothing is
+ *   pushed.  Then scale = s(max(history)), scale_inv = fl32(1 / scale).
+ *   len in [1, 65536]; margin in [0, 64].  One workgroup; device state only. */
+int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* amax, int fmt,
+                            int margin, float* scale, float* scale_inv, int32_t* nonfinite,
+                            void* stream);
+
+/* fp8_gemm_scaled -- C = dequant(A) . dequant(B)^T, FP32 accumulation.
+ * [P1 sec. 3.1: fprop Y = X W, dgrad dX = dY W^T, wgrad dW = X^T dY on
+ *  quantized inputs with BF16/FP32 outputs; P3 Fig. 1 discussion: per-block
+ *  scale factors are applied inside the GEMM]
+ *
+ *   a [M x K] codes (fmt_a), lda; b [N x K] codes (fmt_b), ldb; both with
+ *   the contraction index K contiguous.  c [M x N] (c_dtype), ldc.
+ *   s_a, s_b : dequantisation scales laid out per `recipe` (see FP8MI_GEMM_*;
+ *              grids are dense, row-major).  Block recipes scale K-block kb
+ *              = k / 128 (MX: k / 32); 128x128 tiles of B are indexed
+ *              [n / 128][k / 128].
+ *   C[i][j] = sum_k deq(a[i][k]) * deq(b[j][k]) with deq = dec(code) * scale;
+ *   block recipes accumulate each 128-deep K block in an FP32 partial and
+ *   add scale_a * scale_b * partial to the FP32 accumulator.
+ *   Uses:  fprop  a = X   [M x K], b = W   [N x K];
+ *          dgrad  a = dY  [M x N], b = W^T [K x N]  (contraction over N);
+ *          wgrad  a = dY^T[N x M], b = X^T [K x M]  (contraction over M).
+ * Requirements: M, N, K >= 0; K % 16 == 0; a, b 16-byte aligned,
+ * lda, ldb multiples of 16, lda, ldb >= K; ldc >= N.  K == 0 writes zeros.
+ * Tolerance vs a float64 reference over the dequantized operands:
+ * |C - C_ref| <= 2^-10 sum_k |a b| (+ 2^-8 |C_ref| for BF16 output). */
+int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,
+                    const uint8_t* b, int fmt_b, const void* s_b, int64_t ldb,
+                    int recipe, int64_t M, int64_t N, int64_t K,
+                    void* c, int c_dtype, int64_t ldc, void* stream);
+
+/* Human-readable text of a status code; for FP8MI_ERR_HIP the text of the
+ * last HIP error seen by this thread.  The string is owned by the library. */
+const char* fp8_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MI_H */

@@ -1,0 +1,117 @@
+"""The C-ABI library loads and exports every entry point include/fp8mi.h
+declares; host-side argument validation returns the documented status codes
+before any GPU work (runs without a GPU: only invalid calls are made)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_scaled_quantization_scale_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mi.h")
+
+BAD = 0x1000  # never dereferenced: validation fails before any launch
+GOOD = 0x10000  # 16-byte aligned stand-in pointer
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fp8_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(fm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fm.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (fp8_\w+)$", out, flags=re.M))
+    assert set(_declared()) <= exported
+    assert fm.version() == 100
+    assert fm.status_string(fm.ERR_ALIGN).startswith("pointer")
+
+
+def _q(**kw):
+    args = dict(x=GOOD, x_dtype=fm.IN_BF16, rows=256, cols=256, ld_x=256, recipe=fm.BLOCK_1x128,
+                fmt=fm.E4M3, orient=fm.ROW, margin=0, q_row=GOOD, ld_q_row=256, s_row=GOOD,
+                q_col=None, ld_q_col=0, s_col=None, scale=None, scale_inv=None, amax=None,
+                nonfinite=None, stream=0)
+    args.update(kw)
+    return fm.fp8_quantize(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x_dtype=7), fm.ERR_ENUM),
+    (dict(recipe=9), fm.ERR_ENUM),
+    (dict(fmt=2), fm.ERR_ENUM),
+    (dict(orient=0), fm.ERR_ENUM),
+    (dict(rows=-1), fm.ERR_SHAPE),
+    (dict(margin=65), fm.ERR_SHAPE),
+    (dict(x=None), fm.ERR_NULL),
+    (dict(q_row=None), fm.ERR_NULL),
+    (dict(s_row=None), fm.ERR_NULL),
+    (dict(orient=fm.COL), fm.ERR_NULL),
+    (dict(ld_x=100), fm.ERR_SHAPE),
+    (dict(ld_q_row=128), fm.ERR_SHAPE),
+    (dict(x=GOOD + 8), fm.ERR_ALIGN),
+    (dict(ld_x=260), fm.ERR_ALIGN),
+    (dict(q_row=GOOD + 4), fm.ERR_ALIGN),
+    (dict(ld_q_row=264), fm.ERR_ALIGN),
+    (dict(recipe=fm.TENSOR_CURRENT), fm.ERR_NULL),
+    (dict(recipe=fm.TENSOR_CURRENT, amax=GOOD, scale=GOOD), fm.ERR_NULL),
+    (dict(recipe=fm.TENSOR_DELAYED, amax=GOOD), fm.ERR_NULL),
+    (dict(rows=65536 * 128), fm.ERR_UNSUPPORTED),
+])
+def test_quantize_validation(kw, code):
+    assert _q(**kw) == code
+
+
+def test_quantize_empty_is_ok_without_launch():
+    assert _q(rows=0) == fm.OK
+    assert _q(cols=0, x=None, q_row=None) == fm.OK
+
+
+def _g(**kw):
+    args = dict(a=GOOD, fmt_a=fm.E4M3, s_a=GOOD, lda=256, b=GOOD, fmt_b=fm.E4M3, s_b=GOOD, ldb=256,
+                recipe=fm.GEMM_TENSOR, M=128, N=128, K=256, c=GOOD, c_dtype=fm.OUT_BF16, ldc=128,
+                stream=0)
+    args.update(kw)
+    return fm.fp8_gemm_scaled(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt_a=3), fm.ERR_ENUM),
+    (dict(fmt_b=-1), fm.ERR_ENUM),
+    (dict(recipe=4), fm.ERR_ENUM),
+    (dict(c_dtype=2), fm.ERR_ENUM),
+    (dict(M=-1), fm.ERR_SHAPE),
+    (dict(c=None), fm.ERR_NULL),
+    (dict(a=None), fm.ERR_NULL),
+    (dict(s_b=None), fm.ERR_NULL),
+    (dict(K=200), fm.ERR_SHAPE),
+    (dict(lda=128), fm.ERR_SHAPE),
+    (dict(ldc=100), fm.ERR_SHAPE),
+    (dict(a=GOOD + 1), fm.ERR_ALIGN),
+    (dict(ldb=264 - 4), fm.ERR_ALIGN),
+])
+def test_gemm_validation(kw, code):
+    assert _g(**kw) == code
+
+
+def test_gemm_empty_is_ok_without_launch():
+    assert _g(M=0) == fm.OK
+    assert _g(N=0, c=None) == fm.OK
+
+
+def test_history_validation():
+    f = fm.fp8_amax_history_update
+    assert f(GOOD, GOOD, 200, GOOD, 5, 0, GOOD, GOOD, None, 0) == fm.ERR_ENUM
+    assert f(None, GOOD, 200, GOOD, 0, 0, GOOD, GOOD, None, 0) == fm.ERR_NULL
+    assert f(GOOD, GOOD, 0, GOOD, 0, 0, GOOD, GOOD, None, 0) == fm.ERR_SHAPE
+    assert f(GOOD, GOOD, 200, GOOD, 0, -1, GOOD, GOOD, None, 0) == fm.ERR_SHAPE

@@ -1,0 +1,221 @@
+"""GPU parity of fp8_quantize against the CPU oracle: codes, scales and amax
+bit for bit, for every recipe x orientation x format x input dtype, on seeded
+inputs spanning several 128 x 128 tiles with ragged edges, plus special
+values, and an exhaustive sweep of all 2^32 float32 inputs through both
+encoder paths."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_quantization_scale_amd as fm
+import oracle
+import workloads
+from gpu_util import FMT_NAME, codes, dev, host, need_gpu, parallel_encode, same_f32
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(300, 520), (256, 384), (1, 8), (129, 1000), (64, 40)]
+FORMATS = [fm.E4M3, fm.E5M2]
+DTYPES = [torch.bfloat16, torch.float32]
+
+
+def _input(rows, cols, seed, dtype, specials=False):
+    x = workloads.make(workloads.Tensor("X", rows, cols, "outliers", 1.0, seed, 0.02, 50.0))
+    if specials:
+        x[0, : min(cols, 128)] = 0.0  # an all-zero block
+        if rows > 2 and cols > 2:
+            x[2, 1] = 1e-40  # BF16 subnormal
+            x[1, 2] = -0.0
+    return x.to(dtype)
+
+
+def _oracle_blocks(fmt, xf, recipe, orient):
+    if recipe == fm.BLOCK_1x128:
+        br, bc = (1, 128) if orient == fm.ROW else (128, 1)
+        q, g, _ = oracle.quantize_blocks(fmt, xf, br, bc)
+    elif recipe == fm.BLOCK_128x128:
+        q, g, _ = oracle.quantize_blocks(fmt, xf, 128, 128)
+    else:
+        br, bc = (1, 32) if orient == fm.ROW else (32, 1)
+        q, g, _ = oracle.quantize_mx(fmt, xf, br, bc)
+    return (q, g) if orient == fm.ROW else (q.T, g.T)
+
+
+@pytest.mark.parametrize("recipe", [fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32])
+@pytest.mark.parametrize("orient", [fm.ROW, fm.COL, fm.ROW_AND_COL])
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_block_recipes_match_oracle(recipe, orient, fmt, dtype):
+    need_gpu()
+    for si, (rows, cols) in enumerate(SHAPES):
+        x = _input(rows, cols, 100 + si, dtype, specials=si == 0)
+        xf = x.float().numpy()
+        q = fm.quantize(x.cuda(), recipe, fmt, orient)
+        name = FMT_NAME[fmt]
+        if orient & fm.ROW:
+            oq, og = _oracle_blocks(name, xf, recipe, fm.ROW)
+            assert np.array_equal(codes(q.q_row, rows, cols), oq), (rows, cols)
+            assert np.array_equal(host(q.s_row), og), (rows, cols)
+        if orient & fm.COL:
+            oq, og = _oracle_blocks(name, xf, recipe, fm.COL)
+            assert np.array_equal(codes(q.q_col, cols, rows), oq), (rows, cols)
+            assert np.array_equal(host(q.s_col), og), (rows, cols)
+
+
+@pytest.mark.parametrize("orient", [fm.ROW, fm.COL, fm.ROW_AND_COL])
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_tensor_current_matches_oracle(orient, fmt, dtype):
+    need_gpu()
+    for si, (rows, cols) in enumerate(SHAPES):
+        x = _input(rows, cols, 200 + si, dtype, specials=si == 0)
+        q = fm.quantize(x.cuda(), fm.TENSOR_CURRENT, fmt, orient)
+        oq, s, si_, am, flag = oracle.quantize_current(FMT_NAME[fmt], x.float().numpy())
+        assert same_f32(host(q.amax), [am])
+        assert same_f32(host(q.scale), [s]) and same_f32(host(q.scale_inv), [si_])
+        if orient & fm.ROW:
+            assert np.array_equal(codes(q.q_row, rows, cols), oq)
+        if orient & fm.COL:
+            assert np.array_equal(codes(q.q_col, cols, rows), oq.T)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_tensor_delayed_matches_oracle(fmt, dtype):
+    """A carried-over scale that saturates part of the tensor; amax is
+    max-accumulated across calls until the history update consumes it."""
+    need_gpu()
+    scale = np.float32(300.0 if fmt == fm.E4M3 else 4.0e4)
+    acc = np.float32(0.0)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    s_dev = torch.tensor([scale], device="cuda")
+    for si, (rows, cols) in enumerate(SHAPES):
+        x = _input(rows, cols, 300 + si, dtype, specials=si == 0)
+        q = fm.quantize(x.cuda(), fm.TENSOR_DELAYED, fmt, fm.ROW_AND_COL, scale=s_dev, amax=amax)
+        oq, am = oracle.quantize_delayed(FMT_NAME[fmt], x.float().numpy(), scale)
+        acc = max(acc, am)
+        assert np.array_equal(codes(q.q_row, rows, cols), oq)
+        assert np.array_equal(codes(q.q_col, cols, rows), oq.T)
+        assert same_f32(host(amax), [acc])
+
+
+@pytest.mark.parametrize("recipe", [fm.TENSOR_CURRENT, fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32])
+def test_nonfinite_inputs(recipe):
+    need_gpu()
+    rows, cols = 256, 256
+    x = _input(rows, cols, 400, torch.bfloat16)
+    x[5, 7] = float("nan")
+    x[130, 200] = float("inf")
+    x[131, 3] = float("-inf")
+    xf = x.float().numpy()
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = fm.quantize(x.cuda(), recipe, fm.E4M3, fm.ROW_AND_COL, nonfinite=nf)
+    if recipe == fm.TENSOR_CURRENT:
+        oq, s, si, am, flag = oracle.quantize_current("e4m3", xf)
+        assert np.isnan(host(q.amax)[0]) and host(q.scale)[0] == 1.0
+        assert np.array_equal(codes(q.q_row, rows, cols), oq)
+        assert np.array_equal(codes(q.q_col, cols, rows), oq.T)
+        assert host(nf)[0] == 1
+        return
+    expected = 0
+    for orient in (fm.ROW, fm.COL):
+        oq, og = _oracle_blocks("e4m3", xf, recipe, orient)
+        if orient == fm.ROW:
+            assert np.array_equal(codes(q.q_row, rows, cols), oq)
+            assert np.array_equal(host(q.s_row), og)
+        else:
+            assert np.array_equal(codes(q.q_col, cols, rows), oq)
+            assert np.array_equal(host(q.s_col), og)
+    # one count per scale block with a non-finite amax; a 128x128 tile is one
+    # block shared by both layouts
+    if recipe == fm.BLOCK_1x128:
+        expected = oracle.quantize_blocks("e4m3", xf, 1, 128)[2] + oracle.quantize_blocks("e4m3", xf, 128, 1)[2]
+    elif recipe == fm.BLOCK_128x128:
+        expected = oracle.quantize_blocks("e4m3", xf, 128, 128)[2]
+    else:
+        expected = oracle.quantize_mx("e4m3", xf, 1, 32)[2] + oracle.quantize_mx("e4m3", xf, 32, 1)[2]
+    assert expected > 0 and host(nf)[0] == expected
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_empty_current_writes_unit_scale(fmt):
+    need_gpu()
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    q = fm.quantize(x, fm.TENSOR_CURRENT, fmt, fm.ROW)
+    assert host(q.amax)[0] == 0.0 and host(q.scale)[0] == 1.0 and host(q.scale_inv)[0] == 1.0
+
+
+def test_strided_input_rows():
+    """ld_x larger than cols: only the first cols elements of each row count."""
+    need_gpu()
+    base = _input(200, 384, 500, torch.bfloat16)
+    q = fm.quantize(base.cuda()[:, :264], fm.BLOCK_1x128, fm.E4M3, fm.ROW_AND_COL)
+    xf = base[:, :264].float().numpy()
+    oq, og = _oracle_blocks("e4m3", xf, fm.BLOCK_1x128, fm.ROW)
+    assert np.array_equal(codes(q.q_row, 200, 264), oq) and np.array_equal(host(q.s_row), og)
+    oq, og = _oracle_blocks("e4m3", xf, fm.BLOCK_1x128, fm.COL)
+    assert np.array_equal(codes(q.q_col, 264, 200), oq) and np.array_equal(host(q.s_col), og)
+
+
+def test_deterministic():
+    need_gpu()
+    x = _input(512, 768, 600, torch.bfloat16).cuda()
+    a = fm.quantize(x, fm.MX_1x32, fm.E4M3, fm.ROW_AND_COL)
+    b = fm.quantize(x, fm.MX_1x32, fm.E4M3, fm.ROW_AND_COL)
+    assert torch.equal(a.q_row, b.q_row) and torch.equal(a.q_col, b.q_col)
+    assert torch.equal(a.s_row, b.s_row) and torch.equal(a.s_col, b.s_col)
+
+
+# ---------------------------------------------------------------------------
+# exhaustive encoder sweeps
+# ---------------------------------------------------------------------------
+
+CHUNK = 1 << 26
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_every_fp32_input_safe_path(fmt):
+    """All 2^32 float32 bit patterns cast with scale 1 (delayed recipe, FP32
+    input): the saturating/NaN-handling encoder equals the oracle everywhere."""
+    need_gpu()
+    name = FMT_NAME[fmt]
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    bad = 0
+    for start in range(0, 1 << 32, CHUNK):
+        bits = np.arange(start, start + CHUNK, dtype=np.uint64).astype(np.uint32)
+        v = bits.view(np.float32).reshape(-1, 4096)
+        x = torch.from_numpy(v).cuda()
+        q = fm.quantize(x, fm.TENSOR_DELAYED, fmt, fm.ROW, scale=one, amax=amax)
+        got = host(q.q_row)[:, :4096]
+        bad += int((got != parallel_encode(name, v)).sum())
+        del x, q
+    assert bad == 0
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_every_in_range_fp32_input_fast_path(fmt):
+    """Every float32 with |v| <= max, cast by current scaling with amax = max
+    (s = 1): the convert-only encoder path equals the oracle everywhere."""
+    need_gpu()
+    name = FMT_NAME[fmt]
+    mx = np.float32(oracle.max_value(name))
+    top = int(np.array([mx], np.float32).view(np.uint32)[0])
+    bad = 0
+    for sign in (0, 0x80000000):
+        for start in range(0, top + 1, CHUNK):
+            stop = min(start + CHUNK, top + 1)
+            bits = (np.arange(start, stop, dtype=np.uint64).astype(np.uint32) | sign)
+            n = bits.size
+            cols = 4096
+            rows = (n + cols - 1) // cols
+            pad = np.full(rows * cols, top, np.uint32)  # pad with +max: amax = max -> s = 1
+            pad[:n] = bits
+            v = pad.view(np.float32).reshape(rows, cols)
+            x = torch.from_numpy(v).cuda()
+            q = fm.quantize(x, fm.TENSOR_CURRENT, fmt, fm.ROW)
+            assert host(q.scale)[0] == 1.0
+            got = host(q.q_row)[:, :cols]
+            bad += int((got != parallel_encode(name, v)).sum())
+            del x, q
+    assert bad == 0

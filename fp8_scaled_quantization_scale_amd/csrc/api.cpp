@@ -72,6 +72,8 @@ int check_gemm(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const 
     if (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16) return FP8MI_ERR_ALIGN;
   }
   if (M > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL) return FP8MI_ERR_UNSUPPORTED;
+  // operand panels are addressed with 32-bit buffer offsets
+  if (K > 0 && (lda > (1LL << 22) || ldb > (1LL << 22))) return FP8MI_ERR_UNSUPPORTED;
   return FP8MI_OK;
 }
 

@@ -15,12 +15,16 @@
 // in the last four; K block g (bytes [32g, 32g+32)) takes its E8M0 scale from
 // lane group g.  Result: lane l, register r holds C[4(l/16) + r][l % 16].
 //
-// Tiling: 256 threads = 2 x 2 waves, wave tile WM x WN, workgroup tile
-// (2 WM) x (2 WN), K step 128 (= one block of the 1x128 / 128x128 recipes,
-// = four MX blocks).  A and B tiles are double-buffered in LDS; 16-byte
-// chunks are XOR-swizzled by row so the 16 rows read by one lane group hit
-// distinct banks.  The next K step's global loads are issued before the
-// current step's MFMAs.
+// Data movement: the K loop runs over 128-deep steps (one block of the 1x128 /
+// 128x128 recipes, four MX blocks).  Operand tiles stream HBM -> LDS with
+// buffer_load_dwordx4 ... lds (no VGPR staging): each wave instruction fills
+// 1 KB = 8 tile rows; the lanes fetch permuted 16-byte chunks so that LDS
+// holds every row XOR-swizzled (chunk c of row r at slot c ^ (r & 7)), which
+// keeps the 16 rows one fragment read touches on distinct banks.  Rows past
+// the matrix and K past its end come back as zeros from the buffer's range
+// check, so the loop has no bounds branches.  A ring of STAGES LDS buffers
+// keeps STAGES - 1 steps of loads in flight behind the MFMAs, with one
+// workgroup barrier per step.
 //
 // Scale application:
 //   TENSOR      one alpha = s_a * s_b on the FP32 accumulator at the end;
@@ -36,9 +40,10 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 128;
-constexpr int kThreads = 256;
+constexpr uint32_t kOOB = 0x80000000u;  // voffset past every buffer's range
 
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
@@ -49,6 +54,31 @@ __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One wave-wide 16-byte-per-lane LDS DMA: LDS[m0 + 16 * lane] = buffer[voff + soff].
+// Issued as inline asm so that the compiler's wait-count pass does not treat
+// it as an LDS store aliasing every later LDS read (which would force a full
+// vmcnt(0) drain before each K step's fragment reads and serialise the
+// prefetch); completion is tracked explicitly with wait_vmcnt below.  The
+// s_nop covers the M0-write -> LDS-DMA wait state.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff,
+                                      uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 struct GArgs {
@@ -62,32 +92,44 @@ struct GArgs {
   int tiles_m, tiles_n;
 };
 
-// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `row`.
-__device__ __forceinline__ int swz(int row, int ch) { return row * kBK + ((ch ^ (row & 7)) << 4); }
+template <int REC>
+struct ScaleTraits {
+  // dwords staged per K step for A and for B (float bits or 4 packed E8M0 bytes)
+  template <int BM>
+  static constexpr int a_words() { return REC == kGemmTensor ? 0 : BM; }
+  template <int BN>
+  static constexpr int b_words() {
+    return REC == kGemmTensor ? 0 : (REC == kGemmBlock128x128 ? (BN + 127) / 128 : BN);
+  }
+};
 
-template <int FA, int FB, int REC, int OUT, int WM, int WN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
-  constexpr int BM = 2 * WM, BN = 2 * WN;
+template <int FA, int FB, int REC, int OUT, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p) {
+  constexpr int NTHR = 64 * WAVES_M * WAVES_N;
+  constexpr int NWAVES = WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MT = WM / 16, NT = WN / 16;
-  constexpr int A_LD = BM * 8 / kThreads;  // 16-byte chunks per thread per K step
-  constexpr int B_LD = BN * 8 / kThreads;
+  constexpr int SEG_A = BM / 8, SEG_B = BN / 8;  // 1 KB LDS segments per tile
+  static_assert((SEG_A + SEG_B) % NWAVES == 0, "segments split evenly over waves");
+  constexpr int LOADS = (SEG_A + SEG_B) / NWAVES;  // DMA instructions per wave per K step
+  constexpr int TILE_BYTES = (BM + BN) * kBK;
+  constexpr int SA_W = ScaleTraits<REC>::template a_words<BM>();
+  constexpr int SB_W = ScaleTraits<REC>::template b_words<BN>();
+  constexpr int S_W = SA_W + SB_W;
   constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
-  constexpr int SA_N = (REC == kGemmTensor) ? 1 : BM;  // staged A scales per K step
-  constexpr int SB_N = (REC == kGemmTensor) ? 1 : (REC == kGemmBlock128x128 ? (BN + 127) / 128 : BN);
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kBK];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][SA_N];  // float bits or 4 E8M0 bytes
-  __shared__ __attribute__((aligned(16))) uint32_t lds_sb[2][SB_N];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t sscale[STAGES][S_W > 0 ? S_W : 1];
 
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lr = lane & 15;  // fragment row
   const int lg = lane >> 4;  // lane group
 
-  // ---- tile assignment: XCD-contiguous ranges, then grouped along M
+  // ---- tile assignment: XCD-contiguous ranges of the grid, grouped along M
   int pid = blockIdx.x;
   const int total = p.tiles_m * p.tiles_n;
   if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
@@ -98,97 +140,101 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
   const int pm = first_m + (pid % in_group) % gsize;
   const int pn = (pid % in_group) / gsize;
   const int m0 = pm * BM, n0 = pn * BN;
-
+  const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
   const int KT = (p.K + kBK - 1) / kBK;
 
-  // ---- staging registers for the next K step
-  uint4 ra[A_LD], rb[B_LD];
-  uint32_t rsa = 0, rsb = 0;
+  // ---- buffer resources over this workgroup's row panels of A and B
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
 
-  auto gload = [&](int kt) {
+  // per-lane source offsets of this wave's DMA segments (K step 0)
+  uint32_t voff[LOADS];
+  int kchunk[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int seg = wave * LOADS + i;
+    const int rsub = lane >> 3;                  // row within the 8-row segment
+    const int c = (lane & 7) ^ rsub;             // logical chunk this lane fetches
+    kchunk[i] = 16 * c;
+    if (seg < SEG_A) {
+      voff[i] = (uint32_t)((8 * seg + rsub) * p.lda + 16 * c);
+    } else {
+      voff[i] = (uint32_t)((8 * (seg - SEG_A) + rsub) * p.ldb + 16 * c);
+    }
+  }
+
+  // ---- scales: fetched with range-checked buffer loads (zero past the matrix)
+  // into VGPRs before a step's tile DMAs, written to LDS at the end of the
+  // iteration; every lane issues the same count so vmcnt stays uniform
+  constexpr int SLW = S_W > 0 ? (S_W + NTHR - 1) / NTHR : 0;  // scale words per thread
+  uint32_t rs[SLW > 0 ? SLW : 1];
+  __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
+  int nkb = 0;
+  if constexpr (kBlock) {
+    nkb = KT;
+    rsa = make_rsrc(reinterpret_cast<const uint32_t*>(p.sa) + (int64_t)m0 * nkb, (uint32_t)(rows_a * nkb * 4));
+    if constexpr (REC == kGemmBlock128x128) {
+      const int tb = (rows_b + 127) / 128;
+      rsb = make_rsrc(reinterpret_cast<const uint32_t*>(p.sb) + (int64_t)(n0 / 128) * nkb, (uint32_t)(tb * nkb * 4));
+    } else {
+      rsb = make_rsrc(reinterpret_cast<const uint32_t*>(p.sb) + (int64_t)n0 * nkb, (uint32_t)(rows_b * nkb * 4));
+    }
+  } else if constexpr (REC == kGemmMx) {
+    nkb = (p.K + 31) / 32;
+    rsa = make_rsrc(reinterpret_cast<const uint8_t*>(p.sa) + (int64_t)m0 * nkb, (uint32_t)(rows_a * nkb));
+    rsb = make_rsrc(reinterpret_cast<const uint8_t*>(p.sb) + (int64_t)n0 * nkb, (uint32_t)(rows_b * nkb));
+  }
+
+  auto load_scales = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < SLW; ++i) {
+      const int t = tid + NTHR * i;
+      const bool isa = t < SA_W;
+      const int r = isa ? t : t - SA_W;  // row (or 128-row tile) within the panel
+      if constexpr (kBlock) {
+        const uint32_t off = (t < S_W) ? (uint32_t)((r * nkb + kt) * 4) : kOOB;
+        rs[i] = isa ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0)
+                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsb, off, 0, 0);
+      } else if constexpr (REC == kGemmMx) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kb = 4 * kt + j;
+          const uint32_t off = (t < S_W && kb < nkb) ? (uint32_t)(r * nkb + kb) : kOOB;
+          const uint32_t byte = isa ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0)
+                                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsb, off, 0, 0);
+          w |= byte << (8 * j);
+        }
+        rs[i] = w;
+      }
+    }
+  };
+  auto store_scales = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < SLW; ++i) {
+      const int t = tid + NTHR * i;
+      if (t < S_W) sscale[kt % STAGES][t] = rs[i];
+    }
+  };
+
+  auto issue = [&](int kt) {
+    const int st = kt % STAGES;
     const int k0 = kt * kBK;
+    const uint32_t base = lds_base + st * TILE_BYTES;
+    if constexpr (S_W > 0) load_scales(kt);
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + kThreads * i;
-      const int row = q >> 3, ch = q & 7;
-      const int gm = m0 + row, gk = k0 + 16 * ch;
-      ra[i] = (gm < p.M && gk < p.K) ? *reinterpret_cast<const uint4*>(p.a + (int64_t)gm * p.lda + gk)
-                                     : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int q = tid + kThreads * i;
-      const int row = q >> 3, ch = q & 7;
-      const int gn = n0 + row, gk = k0 + 16 * ch;
-      rb[i] = (gn < p.N && gk < p.K) ? *reinterpret_cast<const uint4*>(p.b + (int64_t)gn * p.ldb + gk)
-                                     : make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (kBlock) {
-      const int kb = kt;  // one 128-deep K block per step
-      const int nkb = KT;
-      if (tid < SA_N) {
-        const int gm = m0 + tid;
-        rsa = gm < p.M ? reinterpret_cast<const uint32_t*>(p.sa)[(int64_t)gm * nkb + kb] : 0u;
-      }
-      if (tid < SB_N) {
-        if constexpr (REC == kGemmBlock128x128) {
-          const int gnb = n0 / 128 + tid;
-          rsb = gnb * 128 < p.N ? reinterpret_cast<const uint32_t*>(p.sb)[(int64_t)gnb * nkb + kb] : 0u;
-        } else {
-          const int gn = n0 + tid;
-          rsb = gn < p.N ? reinterpret_cast<const uint32_t*>(p.sb)[(int64_t)gn * nkb + kb] : 0u;
-        }
-      }
-    } else if constexpr (REC == kGemmMx) {
-      // 4 E8M0 bytes (K blocks 4kt .. 4kt+3) per row, from a [rows x ceil(K/32)] byte grid
-      const int nkb = (p.K + 31) / 32;
-      const int kb0 = kt * 4;
-      if (tid < SA_N) {
-        const int gm = m0 + tid;
-        uint32_t w = 0x7F7F7F7Fu;
-        if (gm < p.M) {
-          const uint8_t* s = reinterpret_cast<const uint8_t*>(p.sa) + (int64_t)gm * nkb;
-          w = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w |= (uint32_t)(kb0 + j < nkb ? s[kb0 + j] : 127) << (8 * j);
-        }
-        rsa = w;
-      }
-      if (tid < SB_N) {
-        const int gn = n0 + tid;
-        uint32_t w = 0x7F7F7F7Fu;
-        if (gn < p.N) {
-          const uint8_t* s = reinterpret_cast<const uint8_t*>(p.sb) + (int64_t)gn * nkb;
-          w = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w |= (uint32_t)(kb0 + j < nkb ? s[kb0 + j] : 127) << (8 * j);
-        }
-        rsb = w;
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const int seg = wave * LOADS + i;
+      const uint32_t vo = (k0 + kchunk[i] < p.K) ? voff[i] : kOOB;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + seg * 1024);
+      dma16(seg < SEG_A ? ra : rb, dst, vo, (uint32_t)k0);
     }
   };
 
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(&lds_a[st][swz(q >> 3, q & 7)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int q = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(&lds_b[st][swz(q >> 3, q & 7)]) = rb[i];
-    }
-    if constexpr (REC != kGemmTensor) {
-      if (tid < SA_N) lds_sa[st][tid] = rsa;
-      if (tid < SB_N) lds_sb[st][tid] = rsb;
-    }
-  };
-
-  // fragment loads: two 16-byte chunks (lane group g: chunks g and 4 + g)
+  // fragment: two 16-byte chunks of tile row `row` (lane group g: chunks g and 4 + g)
   auto frag = [&](const uint8_t* base, int row) -> v8i {
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + swz(row, lg));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + swz(row, 4 + lg));
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kBK + ((lg ^ (row & 7)) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kBK + (((4 + lg) ^ (row & 7)) << 4));
     v8i f;
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
@@ -201,18 +247,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (KT > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-  }
+  // prologue: STAGES - 1 steps in flight
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) {
+      issue(s);
+      if constexpr (S_W > 0) store_scales(s);
+    }
 
   for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+    // this step's DMA done (later steps may still be in flight), then make
+    // every wave's data visible and retire the stage of step kt - 1
+    if (kt + STAGES - 2 < KT)
+      wait_vmcnt<LOADS * (STAGES - 2)>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
 
-    const uint8_t* la = lds_a[st];
-    const uint8_t* lb = lds_b[st];
+    const int st = kt % STAGES;
+    const uint8_t* la = smem + st * TILE_BYTES;
+    const uint8_t* lb = la + BM * kBK;
     v8i fa[MT], fb[NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) fa[i] = frag(la, wm * WM + i * 16 + lr);
@@ -227,9 +282,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
     } else if constexpr (REC == kGemmMx) {
       int sa[MT], sb[NT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) sa[i] = (int)((lds_sa[st][wm * WM + i * 16 + lr] >> (8 * lg)) & 0xFFu);
+      for (int i = 0; i < MT; ++i) sa[i] = (int)((sscale[st][wm * WM + i * 16 + lr] >> (8 * lg)) & 0xFFu);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sb[j] = (int)((lds_sb[st][wn * WN + j * 16 + lr] >> (8 * lg)) & 0xFFu);
+      for (int j = 0; j < NT; ++j) sb[j] = (int)((sscale[st][SA_W + wn * WN + j * 16 + lr] >> (8 * lg)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -239,15 +294,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
       float sa[MT][4];
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&lds_sa[st][wm * WM + i * 16 + 4 * lg]);
+        const uint4 w = *reinterpret_cast<const uint4*>(&sscale[st][wm * WM + i * 16 + 4 * lg]);
         sa[i][0] = __builtin_bit_cast(float, w.x);
         sa[i][1] = __builtin_bit_cast(float, w.y);
         sa[i][2] = __builtin_bit_cast(float, w.z);
         sa[i][3] = __builtin_bit_cast(float, w.w);
       }
       if constexpr (REC == kGemmBlock128x128) {
-        // the wave's WN columns lie inside one 128-wide B tile
-        const float sbv = __builtin_bit_cast(float, lds_sb[st][(wn * WN) / 128]);
+        static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie inside one 128-wide B tile");
+        const float sbv = __builtin_bit_cast(float, sscale[st][SA_W + (wn * WN) / 128]);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -263,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
       } else {
         float sb[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) sb[j] = __builtin_bit_cast(float, lds_sb[st][wn * WN + j * 16 + lr]);
+        for (int j = 0; j < NT; ++j) sb[j] = __builtin_bit_cast(float, sscale[st][SA_W + wn * WN + j * 16 + lr]);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -274,9 +329,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
           }
       }
     }
-
-    if (kt + 1 < KT) sstore(st ^ 1);
-    __syncthreads();
+    if constexpr (S_W > 0)
+      if (kt + STAGES - 1 < KT) store_scales(kt + STAGES - 1);
   }
 
   // ---- epilogue
@@ -306,9 +360,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GArgs p) {
 template <int FA, int FB, int REC, int OUT>
 hipError_t launch4(const GemmParams& g, hipStream_t st) {
   constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
-  constexpr int WM = kBlock ? 64 : 128;
-  constexpr int WN = 128;
-  constexpr int BM = 2 * WM, BN = 2 * WN;
+  // block recipes keep the FP32 accumulator in VGPRs (VALU promotion), so one
+  // wave per SIMD with a 128 x 64 wave tile; the others accumulate inside the
+  // matrix core and run two waves per SIMD
+  constexpr int BM = 256, BN = kBlock ? 128 : 256;
+  constexpr int WAVES_M = 2, WAVES_N = kBlock ? 2 : 4;
+  // two stages: the scale loads of the block / MX recipes are waited on at
+  // the end of each step, which retires that step's tile DMAs as well
+  constexpr int STAGES = 2;
   GArgs a;
   a.a = g.a;
   a.b = g.b;
@@ -324,7 +383,8 @@ hipError_t launch4(const GemmParams& g, hipStream_t st) {
   a.tiles_m = (int)((g.M + BM - 1) / BM);
   a.tiles_n = (int)((g.N + BN - 1) / BN);
   const unsigned blocks = (unsigned)a.tiles_m * (unsigned)a.tiles_n;
-  gemm_kernel<FA, FB, REC, OUT, WM, WN><<<blocks, kThreads, 0, st>>>(a);
+  gemm_kernel<FA, FB, REC, OUT, BM, BN, WAVES_M, WAVES_N, STAGES>
+      <<<blocks, 64 * WAVES_M * WAVES_N, 0, st>>>(a);
   return hipGetLastError();
 }
 

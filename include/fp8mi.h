@@ -172,7 +172,8 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  *          dgrad  a = dY  [M x N], b = W^T [K x N]  (contraction over N);
  *          wgrad  a = dY^T[N x M], b = X^T [K x M]  (contraction over M).
  * Requirements: M, N, K >= 0; K % 16 == 0; a, b 16-byte aligned,
- * lda, ldb multiples of 16, lda, ldb >= K; ldc >= N.  K == 0 writes zeros.
+ * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 (else
+ * FP8MI_ERR_UNSUPPORTED); ldc >= N.  K == 0 writes zeros.
  * Tolerance vs a float64 reference over the dequantized operands:
  * |C - C_ref| <= 2^-10 sum_k |a b| (+ 2^-8 |C_ref| for BF16 output). */
 int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,

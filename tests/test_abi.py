@@ -99,6 +99,7 @@ def _g(**kw):
     (dict(ldc=100), fm.ERR_SHAPE),
     (dict(a=GOOD + 1), fm.ERR_ALIGN),
     (dict(ldb=264 - 4), fm.ERR_ALIGN),
+    (dict(lda=(1 << 22) + 16), fm.ERR_UNSUPPORTED),
 ])
 def test_gemm_validation(kw, code):
     assert _g(**kw) == code

@@ -346,6 +346,17 @@ def _traffic(workload: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def calibrate_copy(nbytes: int):
+    """A plain device-to-device copy of known size: what FETCH_SIZE / WRITE_SIZE
+    read for it scales the counters taken on the path's kernels."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,7 +365,12 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.CONFIGS))
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -19,8 +19,8 @@
 // 128x128 recipes, four MX blocks).  Operand tiles stream HBM -> LDS with
 // buffer_load_dwordx4 ... lds (no VGPR staging): each wave instruction fills
 // 1 KB = 8 tile rows; the lanes fetch permuted 16-byte chunks so that LDS
-// holds every row XOR-swizzled (chunk c of row r at slot c ^ (r & 7)), which
-// keeps the 16 rows one fragment read touches on distinct banks.  Rows past
+// holds every row XOR-swizzled (chunk c of row r at slot c ^ swz(r)), which
+// keeps the rows one fragment read touches on distinct banks.  Rows past
 // the matrix and K past its end come back as zeros from the buffer's range
 // check, so the loop has no bounds branches.  A ring of STAGES LDS buffers
 // keeps STAGES - 1 steps of loads in flight behind the MFMAs, with one
@@ -55,6 +55,14 @@ template <int FA, int FB>
 __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
 }
+
+// LDS chunk swizzles (16-byte chunk c of tile row r lives at slot c ^ swz(r)).
+// A fragments read 16 consecutive rows; B fragments read rows
+// 16 g' + 4 j + (0..3) for g' = 0..3 (see brow).  Each 8-lane phase of a
+// 16-byte LDS read must see 8 distinct slots: rows r..r+7 for A, bits 0, 1
+// and 4 of the row for B.
+__device__ __forceinline__ int swz_a(int row) { return row & 7; }
+__device__ __forceinline__ int swz_b(int row) { return (row & 3) | ((row >> 2) & 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -153,13 +161,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int seg = wave * LOADS + i;
-    const int rsub = lane >> 3;                  // row within the 8-row segment
-    const int c = (lane & 7) ^ rsub;             // logical chunk this lane fetches
-    kchunk[i] = 16 * c;
+    const int rsub = lane >> 3;  // row within the 8-row segment
     if (seg < SEG_A) {
-      voff[i] = (uint32_t)((8 * seg + rsub) * p.lda + 16 * c);
+      const int row = 8 * seg + rsub;
+      const int c = (lane & 7) ^ swz_a(row);  // logical chunk this lane fetches
+      kchunk[i] = 16 * c;
+      voff[i] = (uint32_t)(row * p.lda + 16 * c);
     } else {
-      voff[i] = (uint32_t)((8 * (seg - SEG_A) + rsub) * p.ldb + 16 * c);
+      const int row = 8 * (seg - SEG_A) + rsub;
+      const int c = (lane & 7) ^ swz_b(row);
+      kchunk[i] = 16 * c;
+      voff[i] = (uint32_t)(row * p.ldb + 16 * c);
     }
   }
 
@@ -232,14 +244,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   };
 
   // fragment: two 16-byte chunks of tile row `row` (lane group g: chunks g and 4 + g)
-  auto frag = [&](const uint8_t* base, int row) -> v8i {
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kBK + ((lg ^ (row & 7)) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kBK + (((4 + lg) ^ (row & 7)) << 4));
+  auto frag = [&](const uint8_t* base, int row, int sw) -> v8i {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kBK + ((lg ^ sw) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kBK + (((4 + lg) ^ sw) << 4));
     v8i f;
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
     return f;
   };
+
+  // Row of the wave's B tile that lane row lr loads for sub-tile j: lane group
+  // g' = lr / 4 of the C^T result covers columns [g' * CPL, (g' + 1) * CPL).
+  constexpr int CPL = 4 * NT;  // consecutive C columns per lane
+  auto brow = [&](int j) { return (lr >> 2) * CPL + 4 * j + (lr & 3); };
 
   v4f acc[MT][NT];
 #pragma unroll
@@ -270,62 +287,69 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
     const uint8_t* lb = la + BM * kBK;
     v8i fa[MT], fb[NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) fa[i] = frag(la, wm * WM + i * 16 + lr);
+    for (int i = 0; i < MT; ++i) {
+      const int row = wm * WM + i * 16 + lr;
+      fa[i] = frag(la, row, swz_a(row));
+    }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) fb[j] = frag(lb, wn * WN + j * 16 + lr);
+    for (int j = 0; j < NT; ++j) {
+      const int row = wn * WN + brow(j);
+      fb[j] = frag(lb, row, swz_b(row));
+    }
 
+    // The MFMA computes C^T tiles (B fragment first): lane (lr, lg) then holds
+    // row i*16 + lr and columns lg*CPL + 4j + r of the wave tile.
     if constexpr (REC == kGemmTensor) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FA, FB>(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
     } else if constexpr (REC == kGemmMx) {
       int sa[MT], sb[NT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) sa[i] = (int)((sscale[st][wm * WM + i * 16 + lr] >> (8 * lg)) & 0xFFu);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sb[j] = (int)((sscale[st][SA_W + wn * WN + j * 16 + lr] >> (8 * lg)) & 0xFFu);
+      for (int j = 0; j < NT; ++j) sb[j] = (int)((sscale[st][SA_W + wn * WN + brow(j)] >> (8 * lg)) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma_mx<FA, FB>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma_mx<FB, FA>(fb[j], fa[i], acc[i][j], sb[j], sa[i]);
     } else {
-      // per-row A scales of this lane's four result rows
-      float sa[MT][4];
+      // the A scale of this lane's row in each M sub-tile
+      float sa[MT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&sscale[st][wm * WM + i * 16 + 4 * lg]);
-        sa[i][0] = __builtin_bit_cast(float, w.x);
-        sa[i][1] = __builtin_bit_cast(float, w.y);
-        sa[i][2] = __builtin_bit_cast(float, w.z);
-        sa[i][3] = __builtin_bit_cast(float, w.w);
-      }
+      for (int i = 0; i < MT; ++i) sa[i] = __builtin_bit_cast(float, sscale[st][wm * WM + i * 16 + lr]);
       if constexpr (REC == kGemmBlock128x128) {
         static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie inside one 128-wide B tile");
         const float sbv = __builtin_bit_cast(float, sscale[st][SA_W + (wn * WN) / 128]);
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sa[i][r] *= sbv;
+        for (int i = 0; i < MT; ++i) sa[i] *= sbv;
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
-            const v4f part = mfma<FA, FB>(fa[i], fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            const v4f part = mfma<FB, FA>(fb[j], fa[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[i][r], acc[i][j][r]);
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[i], acc[i][j][r]);
           }
       } else {
-        float sb[NT];
+        // B scales of this lane's 4 NT columns (lg*CPL .. +CPL), 4 per sub-tile
+        float sb[NT][4];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) sb[j] = __builtin_bit_cast(float, sscale[st][SA_W + wn * WN + j * 16 + lr]);
+        for (int j = 0; j < NT; ++j) {
+          const uint4 w = *reinterpret_cast<const uint4*>(&sscale[st][SA_W + wn * WN + lg * CPL + 4 * j]);
+          sb[j][0] = __builtin_bit_cast(float, w.x);
+          sb[j][1] = __builtin_bit_cast(float, w.y);
+          sb[j][2] = __builtin_bit_cast(float, w.z);
+          sb[j][3] = __builtin_bit_cast(float, w.w);
+        }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
-            const v4f part = mfma<FA, FB>(fa[i], fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            const v4f part = mfma<FB, FA>(fb[j], fa[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[i][r] * sb[j], acc[i][j][r]);
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[i] * sb[j][r], acc[i][j][r]);
           }
       }
     }
@@ -333,38 +357,78 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       if (kt + STAGES - 1 < KT) store_scales(kt + STAGES - 1);
   }
 
-  // ---- epilogue
+  // ---- epilogue: each lane writes CPL consecutive columns of its rows with
+  // 16-byte stores (element stores at the matrix edge or for unaligned C)
   float alpha = 1.0f;
   if constexpr (REC == kGemmTensor) {
     if (KT > 0) alpha = *reinterpret_cast<const float*>(p.sa) * *reinterpret_cast<const float*>(p.sb);
   }
+  constexpr int ESIZE = OUT == kOutBf16 ? 2 : 4;
+  const bool vec_ok = ((p.ldc * ESIZE) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
+  const int cbase = n0 + wn * WN + lg * CPL;
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MT; ++i) {
+    const int row = m0 + wm * WM + i * 16 + lr;
+    if (row >= p.M) continue;
+    float v[CPL];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int col = n0 + wn * WN + j * 16 + lr;
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * WM + i * 16 + 4 * lg + r;
-        const float v = (REC == kGemmTensor) ? acc[i][j][r] * alpha : acc[i][j][r];
-        if (row < p.M && col < p.N) {
-          if constexpr (OUT == kOutBf16)
-            reinterpret_cast<__bf16*>(p.c)[(int64_t)row * p.ldc + col] = (__bf16)v;
-          else
-            reinterpret_cast<float*>(p.c)[(int64_t)row * p.ldc + col] = v;
+      for (int r = 0; r < 4; ++r) v[4 * j + r] = (REC == kGemmTensor) ? acc[i][j][r] * alpha : acc[i][j][r];
+    if constexpr (OUT == kOutBf16) {
+      __bf16* dst = reinterpret_cast<__bf16*>(p.c) + (int64_t)row * p.ldc + cbase;
+      if (vec_ok && cbase + CPL <= p.N) {
+#pragma unroll
+        for (int q = 0; q < CPL / 8; ++q) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const __bf16 lo = (__bf16)v[8 * q + 2 * e], hi = (__bf16)v[8 * q + 2 * e + 1];
+            w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          reinterpret_cast<uint4*>(dst)[q] = make_uint4(w[0], w[1], w[2], w[3]);
         }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          if (cbase + c < p.N) dst[c] = (__bf16)v[c];
+      }
+    } else {
+      float* dst = reinterpret_cast<float*>(p.c) + (int64_t)row * p.ldc + cbase;
+      if (vec_ok && cbase + CPL <= p.N) {
+#pragma unroll
+        for (int q = 0; q < CPL / 4; ++q)
+          reinterpret_cast<float4*>(dst)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          if (cbase + c < p.N) dst[c] = v[c];
       }
     }
+  }
 }
+
+// Tile configuration per recipe (measured on MI355X): workgroup tile BM x BN
+// with WAVES_M x WAVES_N waves.
+//   tensor  256x256, 8 waves of 128x64: accumulator inside the matrix core,
+//           two waves per SIMD hide each other's LDS waits;
+//   block   256x128, 8 waves of 64x64: the VGPR accumulator of the promotion
+//           fits two waves per SIMD, so one wave's FMAs overlap the other's MFMAs;
+//   MX      256x256, 4 waves of 128x128: the scale operands push 128x64 waves
+//           past 256 registers, so one wave per SIMD with the full register file.
+template <int REC>
+struct TileCfg {
+  static constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
+  static constexpr int BM = 256;
+  static constexpr int BN = kBlock ? 128 : 256;
+  static constexpr int WAVES_M = kBlock ? 4 : 2;
+  static constexpr int WAVES_N = REC == kGemmTensor ? 4 : 2;
+};
 
 template <int FA, int FB, int REC, int OUT>
 hipError_t launch4(const GemmParams& g, hipStream_t st) {
-  constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
-  // block recipes keep the FP32 accumulator in VGPRs (VALU promotion), so one
-  // wave per SIMD with a 128 x 64 wave tile; the others accumulate inside the
-  // matrix core and run two waves per SIMD
-  constexpr int BM = 256, BN = kBlock ? 128 : 256;
-  constexpr int WAVES_M = 2, WAVES_N = kBlock ? 2 : 4;
+  using C = TileCfg<REC>;
+  constexpr int BM = C::BM, BN = C::BN, WAVES_M = C::WAVES_M, WAVES_N = C::WAVES_N;
   // two stages: the scale loads of the block / MX recipes are waited on at
   // the end of each step, which retires that step's tile DMAs as well
   constexpr int STAGES = 2;

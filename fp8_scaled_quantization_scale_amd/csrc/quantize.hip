@@ -11,8 +11,9 @@
 // (wgrad operands run their blocks along the token dimension M).
 //
 // One kernel handles every recipe and orientation on 128 x 128 tiles:
-//   * each workgroup (256 threads) reads one tile once with 16-byte loads; a
-//     16-lane group owns one tile row per step (16 lanes x 8 elements);
+//   * persistent workgroups (256 threads) walk the tiles, each read once with
+//     16-byte loads while the previous tile is processed; a 16-lane group owns
+//     one tile row per step (16 lanes x 8 elements);
 //   * ROW codes/scales are produced from registers: 1x128 blocks reduce over
 //     the 16 lanes of a group, MX 1x32 blocks over 4 lanes, 128x128 tiles
 //     over the workgroup;
@@ -30,6 +31,19 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+
+// compute units of the current device (queried once per process and device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 enum : int { MODE_TENSOR = 0, MODE_B1x128 = 1, MODE_B128x128 = 2, MODE_MX32 = 3 };
 
@@ -126,204 +140,328 @@ struct TileArgs {
   int margin;
 };
 
-// CURRENT: per-tensor scale from the finished amax; DELAYED: given scale.
+// max |x| key of 8 BF16 values packed in a uint4: packed 16-bit max of the
+// sign-cleared halves (non-negative BF16 orders like its bits, NaN on top).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x8_key(uint4 w) {
+  u16x2 m = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu));
+  const uint32_t k = m.x > m.y ? m.x : m.y;
+  return k << 16;
+}
+
+// A thread's share of one tile: rows g, g+16, ..., g+112, columns
+// [8 li, 8 li + 8) of the tile, as raw 16-byte words (BF16: one per row,
+// FP32: two).  Loads past the tensor's edge are zero.
+template <typename InT>
+struct Raw;
+template <>
+struct Raw<uint16_t> {
+  static constexpr int kWords = 8;
+  uint4 w[8];
+  __device__ __forceinline__ void row(int i, float v[8]) const { unpack_bf16x8(w[i], v); }
+  __device__ __forceinline__ uint32_t key(int i, const float*) const { return bf16x8_key(w[i]); }
+  __device__ __forceinline__ void load(const uint16_t* x, int64_t ld, int64_t rows, int64_t r0, int64_t ccol,
+                                       int64_t nval) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + 16 * i;
+      if (r < rows && nval >= 8) {
+        w[i] = *reinterpret_cast<const uint4*>(x + r * ld + ccol);
+      } else {
+        uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < rows)
+          for (int e = 0; e < 8 && e < nval; ++e) h[e] = x[r * ld + ccol + e];
+        w[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      }
+    }
+  }
+};
+template <>
+struct Raw<float> {
+  static constexpr int kWords = 16;
+  float4 w[16];
+  __device__ __forceinline__ uint32_t key(int, const float* v) const { return max8_key(v); }
+  __device__ __forceinline__ void row(int i, float v[8]) const {
+    v[0] = w[2 * i].x; v[1] = w[2 * i].y; v[2] = w[2 * i].z; v[3] = w[2 * i].w;
+    v[4] = w[2 * i + 1].x; v[5] = w[2 * i + 1].y; v[6] = w[2 * i + 1].z; v[7] = w[2 * i + 1].w;
+  }
+  __device__ __forceinline__ void load(const float* x, int64_t ld, int64_t rows, int64_t r0, int64_t ccol,
+                                       int64_t nval) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + 16 * i;
+      if (r < rows && nval >= 8) {
+        w[2 * i] = reinterpret_cast<const float4*>(x + r * ld + ccol)[0];
+        w[2 * i + 1] = reinterpret_cast<const float4*>(x + r * ld + ccol)[1];
+      } else {
+        float h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < rows)
+          for (int e = 0; e < 8 && e < nval; ++e) h[e] = x[r * ld + ccol + e];
+        w[2 * i] = make_float4(h[0], h[1], h[2], h[3]);
+        w[2 * i + 1] = make_float4(h[4], h[5], h[6], h[7]);
+      }
+    }
+  }
+};
+
+// Delayed scaling: the convert-only encoder is exact for a chunk whose
+// largest magnitude m is finite with fl32(m * s) <= max (every product then
+// rounds to at most max); anything else takes the saturating encoder.
+template <int FMT>
+__device__ __forceinline__ bool fits(uint32_t key, float s) {
+  const float m = key_to_float(key);
+  return m <= kFltMax && m * s <= Fmt<FMT>::kMax;
+}
+
+// Persistent workgroups: each walks tiles blockIdx.x, blockIdx.x + gridDim.x,
+// ... and prefetches the next tile's raw words into registers while the
+// current one is processed, so every workgroup always has a tile in flight.
+// CURRENT: per-tensor scale from the finished amax; otherwise the recipe's own.
 template <typename InT, int FMT, int MODE, bool ROW, bool COL, bool CURRENT>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
   constexpr int kLdsElems = COL ? kTile * kTile : 1;
   __shared__ InT tile[kLdsElems];
   __shared__ uint32_t red4[4];
-  __shared__ uint32_t colred[2][kTile];
+  __shared__ uint32_t colred[4][kTile];
 
   const int tid = threadIdx.x;
   const int g = tid >> 4;   // row group 0..15
   const int li = tid & 15;  // lane in group
-  const int64_t row0 = (int64_t)blockIdx.y * kTile;
-  const int64_t col0 = (int64_t)blockIdx.x * kTile;
-  const int64_t ccol = col0 + 8 * li;  // first column of this lane's chunk
-  const int64_t nval = a.cols - ccol;  // valid elements in the chunk (may be <= 0)
   const InT* x = reinterpret_cast<const InT*>(a.x);
+  const int64_t tiles_x = (a.cols + kTile - 1) / kTile;
+  const int64_t tiles = tiles_x * ((a.rows + kTile - 1) / kTile);
 
-  // ---- load the tile: rows g, g+16, ..., g+112
-  float v[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t r = row0 + g + 16 * i;
-    if (r < a.rows && nval > 0) {
-      load8(x + r * a.ld_x + ccol, nval, v[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-    }
-  }
-
-  // ---- per-tensor and per-tile scales
-  float s_t = 1.0f;
-  bool safe_t = true;
+  // ---- per-tensor scale (the same for every tile)
+  float s_tensor = 1.0f;
+  bool safe_tensor = true;
   if constexpr (MODE == MODE_TENSOR) {
     if constexpr (CURRENT) {
       const float am = *a.amax;
-      s_t = scale_from_amax<FMT>(am, a.margin);
-      safe_t = !is_finite(am);
-      if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-        *a.scale = s_t;
-        *a.scale_inv = recip_rn(s_t);
-        if (safe_t && a.nonfinite) atomicAdd(a.nonfinite, 1);
+      s_tensor = scale_from_amax<FMT>(am, a.margin);
+      safe_tensor = !is_finite(am);
+      if (blockIdx.x == 0 && tid == 0) {
+        *a.scale = s_tensor;
+        *a.scale_inv = recip_rn(s_tensor);
+        if (safe_tensor && a.nonfinite) atomicAdd(a.nonfinite, 1);
       }
     } else {
-      s_t = *a.scale;
+      s_tensor = *a.scale;
+    }
+  }
+  uint32_t amax_acc = 0;  // delayed: this workgroup's running max |x|
+
+  Raw<InT> cur, nxt;
+  int64_t t = blockIdx.x;
+  if (t < tiles) {
+    const int64_t by = t / tiles_x, bx = t - by * tiles_x;
+    cur.load(x, a.ld_x, a.rows, by * kTile + g, bx * kTile + 8 * li, a.cols - (bx * kTile + 8 * li));
+  }
+  for (; t < tiles; t += gridDim.x) {
+    const int64_t by = t / tiles_x, bx = t - by * tiles_x;
+    const int64_t tn = t + gridDim.x;
+    if (tn < tiles) {
+      const int64_t byn = tn / tiles_x, bxn = tn - byn * tiles_x;
+      nxt.load(x, a.ld_x, a.rows, byn * kTile + g, bxn * kTile + 8 * li, a.cols - (bxn * kTile + 8 * li));
+    }
+    const int64_t row0 = by * kTile, col0 = bx * kTile;
+    const int64_t ccol = col0 + 8 * li;  // first column of this lane's chunk
+    const int64_t nval = a.cols - ccol;  // valid elements in the chunk (may be <= 0)
+
+    // ---- per-tile scale (128x128 recipe)
+    float s_t = s_tensor;
+    bool safe_t = safe_tensor;
+    if constexpr (MODE == MODE_B128x128) {
       uint32_t k = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        uint32_t t = max8_key(v[i]);
-        k = k > t ? k : t;
+        float v[8];
+        if constexpr (sizeof(InT) == 4) cur.row(i, v);
+        const uint32_t m = cur.key(i, v);
+        k = k > m ? k : m;
       }
       k = wg_max_u32(k, red4);
-      if (tid == 0) atomicMax(reinterpret_cast<uint32_t*>(a.amax), k);
-    }
-  } else if constexpr (MODE == MODE_B128x128) {
-    uint32_t k = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t t = max8_key(v[i]);
-      k = k > t ? k : t;
-    }
-    k = wg_max_u32(k, red4);
-    const float am = key_to_float(k);
-    s_t = scale_from_amax<FMT>(am, a.margin);
-    safe_t = !is_finite(am);
-    if (tid == 0) {
-      const float si = recip_rn(s_t);
-      const int64_t gr = (a.rows + kTile - 1) / kTile, gc = (a.cols + kTile - 1) / kTile;
-      if (ROW) reinterpret_cast<float*>(a.s_row)[blockIdx.y * gc + blockIdx.x] = si;
-      if (COL) reinterpret_cast<float*>(a.s_col)[blockIdx.x * gr + blockIdx.y] = si;
-      if (safe_t && a.nonfinite) atomicAdd(a.nonfinite, 1);
-    }
-  }
-
-  // ---- ROW layout, straight from registers
-  if constexpr (ROW) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = row0 + g + 16 * i;
-      float s = s_t;
-      bool safe = safe_t;
-      if constexpr (MODE == MODE_B1x128) {
-        const uint32_t k = group_max_u32<16>(max8_key(v[i]));
-        const float am = key_to_float(k);
-        s = scale_from_amax<FMT>(am, a.margin);
-        safe = !is_finite(am);
-        if (li == 0 && r < a.rows) {
-          const int64_t gc = (a.cols + kTile - 1) / kTile;
-          reinterpret_cast<float*>(a.s_row)[r * gc + blockIdx.x] = recip_rn(s);
-          if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
-        }
-      } else if constexpr (MODE == MODE_MX32) {
-        const uint32_t k = group_max_u32<4>(max8_key(v[i]));
-        const int byte = mx_scale_byte<FMT>(key_to_float(k));
-        safe = byte == 0xFF;
-        s = safe ? 1.0f : mx_inv_scale(byte);
-        if ((li & 3) == 0 && r < a.rows && nval > 0) {
-          const int64_t gc = (a.cols + 31) / 32;
-          reinterpret_cast<uint8_t*>(a.s_row)[r * gc + (ccol >> 5)] = (uint8_t)byte;
-          if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
-        }
-      } else if constexpr (MODE == MODE_TENSOR && !CURRENT) {
-        safe = true;
-      }
-      if (r < a.rows && nval > 0) {
-        uint2 c = safe ? encode8<FMT, true>(v[i], s) : encode8<FMT, false>(v[i], s);
-        store8(a.q_row + r * a.ld_q_row + ccol, nval, c);
-      }
-    }
-  }
-
-  // ---- COL layout: transpose through LDS
-  if constexpr (COL) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rl = g + 16 * i;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tile[rl * kTile + 8 * li + e] = In<InT>::from_f(v[i][e]);
-    }
-    __syncthreads();
-
-    const int c = tid & (kTile - 1);  // tile column
-    const int h = tid >> 7;           // rows 64h .. 64h+63
-    const int64_t col = col0 + c;
-    const int64_t rbase = row0 + 64 * h;
-    float w[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j) w[j] = In<InT>::to_f(tile[(64 * h + j) * kTile + c]);
-
-    float s0 = s_t, s1 = s_t;  // scales for rows [0,32) and [32,64) of this half
-    bool safe0 = safe_t, safe1 = safe_t;
-    if constexpr (MODE == MODE_TENSOR && !CURRENT) {
-      safe0 = safe1 = true;
-    } else if constexpr (MODE == MODE_B1x128) {
-      uint32_t k = 0;
-#pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        uint32_t t = abs_key(w[j]);
-        k = k > t ? k : t;
-      }
-      colred[h][c] = k;
-      __syncthreads();
-      k = colred[0][c] > colred[1][c] ? colred[0][c] : colred[1][c];
       const float am = key_to_float(k);
-      s0 = s1 = scale_from_amax<FMT>(am, a.margin);
-      safe0 = safe1 = !is_finite(am);
-      if (h == 0 && col < a.cols) {
+      s_t = scale_from_amax<FMT>(am, a.margin);
+      safe_t = !is_finite(am);
+      if (tid == 0) {
+        const float si = recip_rn(s_t);
         const int64_t gr = (a.rows + kTile - 1) / kTile;
-        reinterpret_cast<float*>(a.s_col)[col * gr + blockIdx.y] = recip_rn(s0);
-        if (safe0 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+        if (ROW) reinterpret_cast<float*>(a.s_row)[by * tiles_x + bx] = si;
+        if (COL) reinterpret_cast<float*>(a.s_col)[bx * gr + by] = si;
+        if (safe_t && a.nonfinite) atomicAdd(a.nonfinite, 1);
       }
-    } else if constexpr (MODE == MODE_MX32) {
-      uint32_t k0 = 0, k1 = 0;
+    }
+
+    // ---- ROW layout, straight from registers
+    if constexpr (ROW) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t r = row0 + g + 16 * i;
+        float v[8];
+        cur.row(i, v);
+        float s = s_t;
+        bool safe = safe_t;
+        if constexpr (MODE == MODE_B1x128) {
+          const uint32_t k = group_max_u32<16>(cur.key(i, v));
+          const float am = key_to_float(k);
+          s = scale_from_amax<FMT>(am, a.margin);
+          safe = !is_finite(am);
+          if (li == 0 && r < a.rows) {
+            reinterpret_cast<float*>(a.s_row)[r * tiles_x + bx] = recip_rn(s);
+            if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
+          }
+        } else if constexpr (MODE == MODE_MX32) {
+          const uint32_t k = group_max_u32<4>(cur.key(i, v));
+          const int byte = mx_scale_byte<FMT>(key_to_float(k));
+          safe = byte == 0xFF;
+          s = safe ? 1.0f : mx_inv_scale(byte);
+          if ((li & 3) == 0 && r < a.rows && nval > 0) {
+            const int64_t gc = (a.cols + 31) / 32;
+            reinterpret_cast<uint8_t*>(a.s_row)[r * gc + (ccol >> 5)] = (uint8_t)byte;
+            if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
+          }
+        } else if constexpr (MODE == MODE_TENSOR && !CURRENT) {
+          const uint32_t k = cur.key(i, v);
+          amax_acc = amax_acc > k ? amax_acc : k;
+          safe = !fits<FMT>(k, s);
+        }
+        if (r < a.rows && nval > 0) {
+          uint2 c = safe ? encode8<FMT, true>(v, s) : encode8<FMT, false>(v, s);
+          store8(a.q_row + r * a.ld_q_row + ccol, nval, c);
+        }
+      }
+    }
+
+    // ---- COL layout: transpose through LDS.  The raw rows go to LDS as they
+    // were loaded; thread (cp, rq) then walks rows [32 rq, 32 rq + 32) of the
+    // column pair (2 cp, 2 cp + 1) with one 4-byte (BF16) or 8-byte (FP32)
+    // read per row, and writes 32 codes of each column as 32 contiguous bytes
+    // of its transposed output row.
+    if constexpr (COL) {
+      __syncthreads();  // the previous tile's column pass is done with `tile`
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rl = g + 16 * i;
+        if constexpr (sizeof(InT) == 2) {
+          reinterpret_cast<uint4*>(tile)[(rl * kTile + 8 * li) / 8] = cur.w[i];
+        } else {
+          reinterpret_cast<float4*>(tile)[(rl * kTile + 8 * li) / 4] = cur.w[2 * i];
+          reinterpret_cast<float4*>(tile)[(rl * kTile + 8 * li) / 4 + 1] = cur.w[2 * i + 1];
+        }
+      }
+      __syncthreads();
+
+      const int cp = tid & 63;  // column pair: tile columns 2cp, 2cp+1
+      const int rq = tid >> 6;  // rows 32rq .. 32rq+31 (one wave per quarter)
+      const int64_t colA = col0 + 2 * cp;
+      const int64_t rbase = row0 + 32 * rq;
+      float w0[32], w1[32];
+      uint32_t k0 = 0, k1 = 0;  // max |x| keys of the two column segments
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        uint32_t t0 = abs_key(w[j]), t1 = abs_key(w[32 + j]);
-        k0 = k0 > t0 ? k0 : t0;
-        k1 = k1 > t1 ? k1 : t1;
-      }
-      const int b0 = mx_scale_byte<FMT>(key_to_float(k0));
-      const int b1 = mx_scale_byte<FMT>(key_to_float(k1));
-      safe0 = b0 == 0xFF;
-      safe1 = b1 == 0xFF;
-      s0 = safe0 ? 1.0f : mx_inv_scale(b0);
-      s1 = safe1 ? 1.0f : mx_inv_scale(b1);
-      if (col < a.cols) {
-        const int64_t gr = (a.rows + 31) / 32;
-        uint8_t* sc = reinterpret_cast<uint8_t*>(a.s_col) + col * gr;
-        if (rbase < a.rows) {
-          sc[rbase >> 5] = (uint8_t)b0;
-          if (safe0 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+        const int rl = 32 * rq + j;
+        if constexpr (sizeof(InT) == 2) {
+          const uint32_t pr = reinterpret_cast<const uint32_t*>(tile)[rl * (kTile / 2) + cp];
+          w0[j] = __builtin_bit_cast(float, pr << 16);
+          w1[j] = __builtin_bit_cast(float, pr & 0xFFFF0000u);
+        } else {
+          const float2 pr = reinterpret_cast<const float2*>(tile)[rl * (kTile / 2) + cp];
+          w0[j] = pr.x;
+          w1[j] = pr.y;
         }
-        if (rbase + 32 < a.rows) {
-          sc[(rbase >> 5) + 1] = (uint8_t)b1;
-          if (safe1 && a.nonfinite) atomicAdd(a.nonfinite, 1);
-        }
+        const uint32_t a0 = abs_key(w0[j]), a1 = abs_key(w1[j]);
+        k0 = k0 > a0 ? k0 : a0;
+        k1 = k1 > a1 ? k1 : a1;
       }
-    }
 
-    if (col < a.cols && rbase < a.rows) {
-      uint32_t pk[16];
+      float s0 = s_t, s1 = s_t;  // scales of the two columns
+      bool safe0 = safe_t, safe1 = safe_t;
+      if constexpr (MODE == MODE_TENSOR && !CURRENT) {
+        if constexpr (!ROW) {
+          const uint32_t m = k0 > k1 ? k0 : k1;
+          amax_acc = amax_acc > m ? amax_acc : m;
+        }
+        safe0 = !fits<FMT>(k0, s_t);
+        safe1 = !fits<FMT>(k1, s_t);
+      } else if constexpr (MODE == MODE_B1x128) {
+        colred[rq][2 * cp] = k0;
+        colred[rq][2 * cp + 1] = k1;
+        __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float s = q < 8 ? s0 : s1;
-        const bool safe = q < 8 ? safe0 : safe1;
-        pk[q] = safe ? encode4<FMT, true>(w[4 * q] * s, w[4 * q + 1] * s, w[4 * q + 2] * s, w[4 * q + 3] * s)
-                     : encode4<FMT, false>(w[4 * q] * s, w[4 * q + 1] * s, w[4 * q + 2] * s, w[4 * q + 3] * s);
+        for (int q = 0; q < 4; ++q) {
+          k0 = k0 > colred[q][2 * cp] ? k0 : colred[q][2 * cp];
+          k1 = k1 > colred[q][2 * cp + 1] ? k1 : colred[q][2 * cp + 1];
+        }
+        const float am0 = key_to_float(k0), am1 = key_to_float(k1);
+        s0 = scale_from_amax<FMT>(am0, a.margin);
+        s1 = scale_from_amax<FMT>(am1, a.margin);
+        safe0 = !is_finite(am0);
+        safe1 = !is_finite(am1);
+        if (rq == 0) {
+          const int64_t gr = (a.rows + kTile - 1) / kTile;
+          if (colA < a.cols) {
+            reinterpret_cast<float*>(a.s_col)[colA * gr + by] = recip_rn(s0);
+            if (safe0 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+          }
+          if (colA + 1 < a.cols) {
+            reinterpret_cast<float*>(a.s_col)[(colA + 1) * gr + by] = recip_rn(s1);
+            if (safe1 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+          }
+        }
+      } else if constexpr (MODE == MODE_MX32) {
+        const int b0 = mx_scale_byte<FMT>(key_to_float(k0));
+        const int b1 = mx_scale_byte<FMT>(key_to_float(k1));
+        safe0 = b0 == 0xFF;
+        safe1 = b1 == 0xFF;
+        s0 = safe0 ? 1.0f : mx_inv_scale(b0);
+        s1 = safe1 ? 1.0f : mx_inv_scale(b1);
+        if (rbase < a.rows) {
+          const int64_t gr = (a.rows + 31) / 32;
+          uint8_t* sc = reinterpret_cast<uint8_t*>(a.s_col);
+          if (colA < a.cols) {
+            sc[colA * gr + (rbase >> 5)] = (uint8_t)b0;
+            if (safe0 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+          }
+          if (colA + 1 < a.cols) {
+            sc[(colA + 1) * gr + (rbase >> 5)] = (uint8_t)b1;
+            if (safe1 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+          }
+        }
       }
-      uint8_t* dst = a.q_col + col * a.ld_q_col + rbase;
-      const int64_t n = a.rows - rbase;
-      if (n >= 64) {
-        uint4* d4 = reinterpret_cast<uint4*>(dst);
+
+      if (rbase < a.rows) {
+        const int64_t n = a.rows - rbase;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d4[q] = make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
-      } else {
-        for (int j = 0; j < n; ++j) dst[j] = (uint8_t)((pk[j >> 2] >> (8 * (j & 3))) & 0xFF);
+        for (int half = 0; half < 2; ++half) {
+          const int64_t col = colA + half;
+          if (col >= a.cols) continue;
+          const float* w = half ? w1 : w0;
+          const float s = half ? s1 : s0;
+          const bool safe = half ? safe1 : safe0;
+          uint32_t pk[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            pk[q] = safe ? encode4<FMT, true>(w[4 * q] * s, w[4 * q + 1] * s, w[4 * q + 2] * s, w[4 * q + 3] * s)
+                         : encode4<FMT, false>(w[4 * q] * s, w[4 * q + 1] * s, w[4 * q + 2] * s, w[4 * q + 3] * s);
+          uint8_t* dst = a.q_col + col * a.ld_q_col + rbase;
+          if (n >= 32) {
+            reinterpret_cast<uint4*>(dst)[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            reinterpret_cast<uint4*>(dst)[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+          } else {
+            for (int j = 0; j < n; ++j) dst[j] = (uint8_t)((pk[j >> 2] >> (8 * (j & 3))) & 0xFF);
+          }
+        }
       }
     }
+    cur = nxt;
+  }
+
+  if constexpr (MODE == MODE_TENSOR && !CURRENT) {
+    const uint32_t k = wg_max_u32(amax_acc, red4);
+    if (tid == 0 && k != 0) atomicMax(reinterpret_cast<uint32_t*>(a.amax), k);
   }
 }
 
@@ -333,39 +471,113 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
 // ---------------------------------------------------------------------------
 __global__ void zero_kernel(float* p) { *p = 0.0f; }
 
+// max |x| key of 8 consecutive elements (fewer at a ragged row end)
+__device__ __forceinline__ uint32_t chunk_key(const uint16_t* p, int64_t n) {
+  if (n >= 8) return bf16x8_key(*reinterpret_cast<const uint4*>(p));
+  float v[8];
+  load8(p, n, v);
+  return max8_key(v);
+}
+__device__ __forceinline__ uint32_t chunk_key(const float* p, int64_t n) {
+  float v[8];
+  load8(p, n, v);
+  return max8_key(v);
+}
+
+// Rows stride over blockIdx.y, 8-element chunks of a row over
+// blockIdx.x * 256 + tid; four rows per trip keep four loads in flight.
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* x, int64_t rows, int64_t cols,
                                                         int64_t ld, float* amax) {
   __shared__ uint32_t red4[4];
   const int64_t cpr = (cols + 7) / 8;
-  const int64_t total = rows * cpr;
   uint32_t k = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = i / cpr;
-    const int64_t cc = (i - r * cpr) * 8;
-    float v[8];
-    load8(x + r * ld + cc, cols - cc, v);
-    const uint32_t t = max8_key(v);
-    k = k > t ? k : t;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < cpr; c += (int64_t)gridDim.x * kThreads) {
+    const int64_t cc = 8 * c;
+    int64_t r = blockIdx.y;
+    for (; r + 3 * (int64_t)gridDim.y < rows; r += 4 * (int64_t)gridDim.y) {
+      const uint32_t k0 = chunk_key(x + r * ld + cc, cols - cc);
+      const uint32_t k1 = chunk_key(x + (r + gridDim.y) * ld + cc, cols - cc);
+      const uint32_t k2 = chunk_key(x + (r + 2 * (int64_t)gridDim.y) * ld + cc, cols - cc);
+      const uint32_t k3 = chunk_key(x + (r + 3 * (int64_t)gridDim.y) * ld + cc, cols - cc);
+      const uint32_t a = k0 > k1 ? k0 : k1, b = k2 > k3 ? k2 : k3;
+      const uint32_t m = a > b ? a : b;
+      k = k > m ? k : m;
+    }
+    for (; r < rows; r += gridDim.y) {
+      const uint32_t m = chunk_key(x + r * ld + cc, cols - cc);
+      k = k > m ? k : m;
+    }
   }
   k = wg_max_u32(k, red4);
-  if (threadIdx.x == 0) atomicMax(reinterpret_cast<uint32_t*>(amax), k);
+  if (threadIdx.x == 0 && k != 0) atomicMax(reinterpret_cast<uint32_t*>(amax), k);
+}
+
+// Contiguous tensors (ld == cols): one flat stream of 8-element chunks,
+// grid-strided with four independent 16-byte loads per trip.
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64_t n, float* amax) {
+  __shared__ uint32_t red4[4];
+  const int64_t nch = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t k = 0;
+  for (; i + 3 * stride < nch; i += 4 * stride) {
+    const uint32_t k0 = chunk_key(x + 8 * i, 8);
+    const uint32_t k1 = chunk_key(x + 8 * (i + stride), 8);
+    const uint32_t k2 = chunk_key(x + 8 * (i + 2 * stride), 8);
+    const uint32_t k3 = chunk_key(x + 8 * (i + 3 * stride), 8);
+    const uint32_t a = k0 > k1 ? k0 : k1, b = k2 > k3 ? k2 : k3;
+    const uint32_t m = a > b ? a : b;
+    k = k > m ? k : m;
+  }
+  for (; i < nch; i += stride) {
+    const uint32_t m = chunk_key(x + 8 * i, 8);
+    k = k > m ? k : m;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n > 8 * nch) {
+    const uint32_t m = chunk_key(x + 8 * nch, n - 8 * nch);
+    k = k > m ? k : m;
+  }
+  k = wg_max_u32(k, red4);
+  if (threadIdx.x == 0 && k != 0) atomicMax(reinterpret_cast<uint32_t*>(amax), k);
+}
+
+// Persistent grid: as many workgroups as stay resident (per the kernel's
+// register / LDS occupancy), rounded so every workgroup walks the same number
+// of tiles.
+template <typename Kernel>
+unsigned persistent_grid(Kernel k, int64_t tiles, int* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int per_cu = cache[dev];
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    cache[dev] = per_cu;
+  }
+  const int64_t resident = (int64_t)cu_count() * per_cu;
+  const int64_t rounds = (tiles + resident - 1) / resident;
+  return (unsigned)((tiles + rounds - 1) / rounds);
+}
+
+template <typename InT, int FMT, int MODE, bool ROW, bool COL, bool CURRENT>
+hipError_t launch_tile_k(const TileArgs& a, int64_t tiles, hipStream_t st) {
+  static int occupancy[64] = {0};  // workgroups per CU, per device
+  auto k = quant_tile_kernel<InT, FMT, MODE, ROW, COL, CURRENT>;
+  k<<<persistent_grid(k, tiles, occupancy), kThreads, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <typename InT, int FMT, int MODE, bool CURRENT>
 hipError_t launch_tile(const QuantParams& p, hipStream_t st) {
   TileArgs a{p.x, p.rows, p.cols, p.ld_x, p.q_row, p.ld_q_row, p.s_row, p.q_col, p.ld_q_col,
              p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin};
-  dim3 grid((unsigned)((p.cols + kTile - 1) / kTile), (unsigned)((p.rows + kTile - 1) / kTile));
+  const int64_t tiles = ((p.cols + kTile - 1) / kTile) * ((p.rows + kTile - 1) / kTile);
   const bool row = p.orient & 1, col = p.orient & 2;
-  if (row && col)
-    quant_tile_kernel<InT, FMT, MODE, true, true, CURRENT><<<grid, kThreads, 0, st>>>(a);
-  else if (row)
-    quant_tile_kernel<InT, FMT, MODE, true, false, CURRENT><<<grid, kThreads, 0, st>>>(a);
-  else
-    quant_tile_kernel<InT, FMT, MODE, false, true, CURRENT><<<grid, kThreads, 0, st>>>(a);
-  return hipGetLastError();
+  if (row && col) return launch_tile_k<InT, FMT, MODE, true, true, CURRENT>(a, tiles, st);
+  if (row) return launch_tile_k<InT, FMT, MODE, true, false, CURRENT>(a, tiles, st);
+  return launch_tile_k<InT, FMT, MODE, false, true, CURRENT>(a, tiles, st);
 }
 
 template <typename InT, int FMT>
@@ -374,11 +586,23 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
     case kRecipeTensorCurrent: {
       zero_kernel<<<1, 1, 0, st>>>(p.amax);
       if (p.rows > 0 && p.cols > 0) {
-        const int64_t chunks = p.rows * ((p.cols + 7) / 8);
-        int64_t blocks = (chunks + kThreads - 1) / kThreads;
-        blocks = blocks < 2048 ? blocks : 2048;
-        amax_kernel<InT><<<(unsigned)blocks, kThreads, 0, st>>>(
-            reinterpret_cast<const InT*>(p.x), p.rows, p.cols, p.ld_x, p.amax);
+        const InT* x = reinterpret_cast<const InT*>(p.x);
+        if (p.ld_x == p.cols || p.rows == 1) {
+          const int64_t n = p.rows * p.cols;
+          int64_t blocks = (n / 8 + kThreads - 1) / kThreads;
+          const int64_t cap = (int64_t)cu_count() * 8;
+          blocks = blocks < cap ? blocks : cap;
+          amax_flat_kernel<InT><<<(unsigned)(blocks > 0 ? blocks : 1), kThreads, 0, st>>>(x, n, p.amax);
+        } else {
+          const int64_t cpr = (p.cols + 7) / 8;
+          int64_t gx = (cpr + kThreads - 1) / kThreads;
+          gx = gx < 64 ? gx : 64;
+          int64_t gy = (int64_t)cu_count() * 8 / gx;
+          gy = gy < p.rows ? gy : p.rows;
+          gy = gy < 65535 ? gy : 65535;
+          amax_kernel<InT><<<dim3((unsigned)gx, (unsigned)(gy > 0 ? gy : 1)), kThreads, 0, st>>>(
+              x, p.rows, p.cols, p.ld_x, p.amax);
+        }
         return launch_tile<InT, FMT, MODE_TENSOR, true>(p, st);
       }
       // empty tensor: amax = 0 -> scale = scale_inv = 1

@@ -208,7 +208,7 @@ def test_every_in_range_fp32_input_fast_path(fmt):
             bits = (np.arange(start, stop, dtype=np.uint64).astype(np.uint32) | sign)
             n = bits.size
             cols = 4096
-            rows = (n + cols - 1) // cols
+            rows = n // cols + 1  # at least one padding element
             pad = np.full(rows * cols, top, np.uint32)  # pad with +max: amax = max -> s = 1
             pad[:n] = bits
             v = pad.view(np.float32).reshape(rows, cols)

@@ -31,6 +31,7 @@ OUT_BF16, OUT_FP32 = 0, 1
 TENSOR_CURRENT, TENSOR_DELAYED, BLOCK_1x128, BLOCK_128x128, MX_1x32 = 0, 1, 2, 3, 4
 ROW, COL, ROW_AND_COL = 1, 2, 3
 GEMM_TENSOR, GEMM_BLOCK_1x128_128x128, GEMM_BLOCK_1x128_1x128, GEMM_MX_1x32 = 0, 1, 2, 3
+AMAX_SLOTS = 1024  # floats in a delayed-scaling amax accumulator
 
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
 TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
@@ -189,7 +190,11 @@ def quantize(x: torch.Tensor, recipe: int, fmt: int, orient: int = ROW, margin: 
         out.scale = scale if scale is not None else torch.ones(1, dtype=torch.float32, device=dev)
         if recipe == TENSOR_CURRENT:  # delayed leaves scale_inv to the history update
             out.scale_inv = torch.empty(1, dtype=torch.float32, device=dev)
-        out.amax = amax if amax is not None else torch.zeros(1, dtype=torch.float32, device=dev)
+        if amax is None:
+            amax = torch.zeros(AMAX_SLOTS if recipe == TENSOR_DELAYED else 1, dtype=torch.float32, device=dev)
+        if recipe == TENSOR_DELAYED and amax.numel() < AMAX_SLOTS:
+            raise Fp8Error(f"a delayed-scaling amax accumulator holds {AMAX_SLOTS} floats")
+        out.amax = amax
     out.nonfinite = nonfinite
     st = fp8_quantize(x, x_dtype, rows, cols, x.stride(0), recipe, fmt, orient, margin,
                       out.q_row, ld_r, out.s_row, out.q_col, ld_c, out.s_col,
@@ -216,7 +221,8 @@ def gemm(a: torch.Tensor, fmt_a: int, s_a: torch.Tensor, b: torch.Tensor, fmt_b:
 
 class DelayedState:
     """Device-resident delayed-scaling state: amax ring, head, scale,
-    scale_inv, the amax accumulator and a non-finite counter."""
+    scale_inv, the amax accumulator (AMAX_SLOTS per-workgroup slots, folded
+    by the history update) and a non-finite counter."""
 
     def __init__(self, fmt: int, length: int = 200, margin: int = 0, device="cuda"):
         self.fmt, self.length, self.margin = fmt, length, margin
@@ -224,7 +230,7 @@ class DelayedState:
         self.head = torch.zeros(1, dtype=torch.int32, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
         self.scale_inv = torch.ones(1, dtype=torch.float32, device=device)
-        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self.amax = torch.zeros(AMAX_SLOTS, dtype=torch.float32, device=device)
         self.nonfinite = torch.zeros(1, dtype=torch.int32, device=device)
 
     def quantize(self, x: torch.Tensor, orient: int = ROW, stream=None) -> Quantized:

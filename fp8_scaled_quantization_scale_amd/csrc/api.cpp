@@ -127,6 +127,6 @@ const char* fp8_status_string(int status) {
   return "unknown status";
 }
 
-int fp8_version(void) { return 100; }
+int fp8_version(void) { return 200; }
 
 }  // extern "C"

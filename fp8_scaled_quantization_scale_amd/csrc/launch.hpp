@@ -13,6 +13,8 @@ constexpr int kOutBf16 = 0, kOutFp32 = 1;
 constexpr int kRecipeTensorCurrent = 0, kRecipeTensorDelayed = 1, kRecipeBlock1x128 = 2,
               kRecipeBlock128x128 = 3, kRecipeMx1x32 = 4;
 constexpr int kGemmTensor = 0, kGemmBlock128x128 = 1, kGemmBlock1x128 = 2, kGemmMx = 3;
+// slots of a delayed-scaling amax accumulator (FP8MI_AMAX_SLOTS)
+constexpr int kAmaxSlots = 1024;
 
 struct QuantParams {
   const void* x;
@@ -48,7 +50,7 @@ struct GemmParams {
 };
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t st);
-hipError_t launch_empty_scale(float* scale, float* scale_inv, hipStream_t st);
+hipError_t launch_empty_scale(float* amax, float* scale, float* scale_inv, hipStream_t st);
 hipError_t launch_history(float* history, int32_t* head, int len, float* amax, int fmt, int margin,
                           float* scale, float* scale_inv, int32_t* nonfinite, hipStream_t st);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st);

@@ -21,7 +21,11 @@
 //     thread walks half a column (64 rows), and the codes of 64 consecutive
 //     rows leave as 64 contiguous bytes of the transposed output row.
 // Per-tensor current scaling needs the amax of the whole tensor before any
-// cast, so it runs a separate reduction kernel first.
+// cast: a reduction pass leaves one partial maximum per workgroup, a
+// one-workgroup pass folds them into *amax, then the cast runs.  No kernel
+// combines results across workgroups with atomics: on MI355X atomics on one
+// address serialise (about 14 ns each), which for a thousand workgroups
+// costs as much as the whole cast.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -135,7 +139,7 @@ struct TileArgs {
   void* s_col;
   float* scale;       // per-tensor: in (delayed) / out (current)
   float* scale_inv;   // per-tensor current: out
-  float* amax;        // per-tensor: in (current) / max-accumulated (delayed)
+  float* amax;        // per-tensor: in (current) / slot accumulator (delayed)
   int32_t* nonfinite;
   int margin;
 };
@@ -251,7 +255,13 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
       s_tensor = *a.scale;
     }
   }
-  uint32_t amax_acc = 0;  // delayed: this workgroup's running max |x|
+  // delayed: this workgroup's running max |x|, seeded with its slot of the
+  // accumulator (slot blockIdx.x belongs to this workgroup alone; the grid
+  // never exceeds kAmaxSlots)
+  uint32_t amax_acc = 0;
+  if constexpr (MODE == MODE_TENSOR && !CURRENT) {
+    if (tid == 0) amax_acc = reinterpret_cast<const uint32_t*>(a.amax)[blockIdx.x];
+  }
 
   Raw<InT> cur, nxt;
   int64_t t = blockIdx.x;
@@ -461,15 +471,33 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
 
   if constexpr (MODE == MODE_TENSOR && !CURRENT) {
     const uint32_t k = wg_max_u32(amax_acc, red4);
-    if (tid == 0 && k != 0) atomicMax(reinterpret_cast<uint32_t*>(a.amax), k);
+    if (tid == 0) reinterpret_cast<uint32_t*>(a.amax)[blockIdx.x] = k;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Per-tensor amax for current scaling: max |x| over the tensor, NaN-dominant,
-// max-accumulated into *amax (zeroed by zero_kernel first).
+// Per-tensor amax for current scaling: max |x| over the tensor, NaN-dominant.
+// Each workgroup of the reduction pass stores its partial maximum (a |x| bit
+// pattern) in a 4-byte slot laid over the code output, which the cast pass
+// overwrites afterwards: slot p sits in output row p / per_row at byte
+// 4 (p % per_row).  A single-workgroup pass stores straight to *amax.
 // ---------------------------------------------------------------------------
-__global__ void zero_kernel(float* p) { *p = 0.0f; }
+struct Slots {
+  uint8_t* base;
+  int64_t ld;       // bytes between output rows
+  int64_t per_row;  // slots per output row (row length / 4)
+  __device__ __forceinline__ uint32_t* at(int64_t p) const {
+    return reinterpret_cast<uint32_t*>(base + (p / per_row) * ld + 4 * (p % per_row));
+  }
+};
+
+__device__ __forceinline__ void put_partial(uint32_t k, const Slots& sl, float* amax) {
+  const int64_t p = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  if (gridDim.x * gridDim.y == 1)
+    *reinterpret_cast<uint32_t*>(amax) = k;
+  else
+    *sl.at(p) = k;
+}
 
 // max |x| key of 8 consecutive elements (fewer at a ragged row end)
 __device__ __forceinline__ uint32_t chunk_key(const uint16_t* p, int64_t n) {
@@ -488,7 +516,7 @@ __device__ __forceinline__ uint32_t chunk_key(const float* p, int64_t n) {
 // blockIdx.x * 256 + tid; four rows per trip keep four loads in flight.
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* x, int64_t rows, int64_t cols,
-                                                        int64_t ld, float* amax) {
+                                                        int64_t ld, Slots sl, float* amax) {
   __shared__ uint32_t red4[4];
   const int64_t cpr = (cols + 7) / 8;
   uint32_t k = 0;
@@ -510,13 +538,13 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* x, int64_t ro
     }
   }
   k = wg_max_u32(k, red4);
-  if (threadIdx.x == 0 && k != 0) atomicMax(reinterpret_cast<uint32_t*>(amax), k);
+  if (threadIdx.x == 0) put_partial(k, sl, amax);
 }
 
 // Contiguous tensors (ld == cols): one flat stream of 8-element chunks,
 // grid-strided with four independent 16-byte loads per trip.
 template <typename InT>
-__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64_t n, float* amax) {
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64_t n, Slots sl, float* amax) {
   __shared__ uint32_t red4[4];
   const int64_t nch = n / 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -540,7 +568,19 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64
     k = k > m ? k : m;
   }
   k = wg_max_u32(k, red4);
-  if (threadIdx.x == 0 && k != 0) atomicMax(reinterpret_cast<uint32_t*>(amax), k);
+  if (threadIdx.x == 0) put_partial(k, sl, amax);
+}
+
+// One workgroup: *amax = max over the `count` partial slots.
+__global__ __launch_bounds__(kThreads) void amax_finalize_kernel(Slots sl, int64_t count, float* amax) {
+  __shared__ uint32_t red4[4];
+  uint32_t k = 0;
+  for (int64_t p = threadIdx.x; p < count; p += kThreads) {
+    const uint32_t v = *sl.at(p);
+    k = k > v ? k : v;
+  }
+  k = wg_max_u32(k, red4);
+  if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(amax) = k;
 }
 
 // Persistent grid: as many workgroups as stay resident (per the kernel's
@@ -565,7 +605,10 @@ template <typename InT, int FMT, int MODE, bool ROW, bool COL, bool CURRENT>
 hipError_t launch_tile_k(const TileArgs& a, int64_t tiles, hipStream_t st) {
   static int occupancy[64] = {0};  // workgroups per CU, per device
   auto k = quant_tile_kernel<InT, FMT, MODE, ROW, COL, CURRENT>;
-  k<<<persistent_grid(k, tiles, occupancy), kThreads, 0, st>>>(a);
+  unsigned grid = persistent_grid(k, tiles, occupancy);
+  // delayed scaling: one accumulator slot per workgroup
+  if (MODE == MODE_TENSOR && !CURRENT && grid > (unsigned)kAmaxSlots) grid = kAmaxSlots;
+  k<<<grid, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -584,29 +627,40 @@ template <typename InT, int FMT>
 hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
   switch (p.recipe) {
     case kRecipeTensorCurrent: {
-      zero_kernel<<<1, 1, 0, st>>>(p.amax);
       if (p.rows > 0 && p.cols > 0) {
         const InT* x = reinterpret_cast<const InT*>(p.x);
+        // partial-maximum slots over the first code output
+        const bool row = p.orient & 1;
+        Slots sl{row ? p.q_row : p.q_col, row ? p.ld_q_row : p.ld_q_col, (row ? p.cols : p.rows) / 4};
+        const int64_t cap_slots = sl.per_row * (row ? p.rows : p.cols);
+        int64_t cap = (int64_t)cu_count() * 8;
+        cap = cap < cap_slots ? cap : cap_slots;
+        cap = cap > 1 ? cap : 1;
+        int64_t parts;
         if (p.ld_x == p.cols || p.rows == 1) {
           const int64_t n = p.rows * p.cols;
           int64_t blocks = (n / 8 + kThreads - 1) / kThreads;
-          const int64_t cap = (int64_t)cu_count() * 8;
           blocks = blocks < cap ? blocks : cap;
-          amax_flat_kernel<InT><<<(unsigned)(blocks > 0 ? blocks : 1), kThreads, 0, st>>>(x, n, p.amax);
+          parts = blocks > 0 ? blocks : 1;
+          amax_flat_kernel<InT><<<(unsigned)parts, kThreads, 0, st>>>(x, n, sl, p.amax);
         } else {
           const int64_t cpr = (p.cols + 7) / 8;
           int64_t gx = (cpr + kThreads - 1) / kThreads;
           gx = gx < 64 ? gx : 64;
-          int64_t gy = (int64_t)cu_count() * 8 / gx;
+          gx = gx < cap ? gx : cap;
+          int64_t gy = cap / gx;
           gy = gy < p.rows ? gy : p.rows;
           gy = gy < 65535 ? gy : 65535;
-          amax_kernel<InT><<<dim3((unsigned)gx, (unsigned)(gy > 0 ? gy : 1)), kThreads, 0, st>>>(
-              x, p.rows, p.cols, p.ld_x, p.amax);
+          gy = gy > 0 ? gy : 1;
+          parts = gx * gy;
+          amax_kernel<InT><<<dim3((unsigned)gx, (unsigned)gy), kThreads, 0, st>>>(x, p.rows, p.cols, p.ld_x,
+                                                                                  sl, p.amax);
         }
+        if (parts > 1) amax_finalize_kernel<<<1, kThreads, 0, st>>>(sl, parts, p.amax);
         return launch_tile<InT, FMT, MODE_TENSOR, true>(p, st);
       }
       // empty tensor: amax = 0 -> scale = scale_inv = 1
-      return launch_empty_scale(p.scale, p.scale_inv, st);
+      return launch_empty_scale(p.amax, p.scale, p.scale_inv, st);
     }
     case kRecipeTensorDelayed:
       if (p.rows == 0 || p.cols == 0) return hipGetLastError();
@@ -621,15 +675,16 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-__global__ void empty_scale_kernel(float* scale, float* scale_inv) {
+__global__ void empty_scale_kernel(float* amax, float* scale, float* scale_inv) {
+  *amax = 0.0f;
   *scale = 1.0f;
   *scale_inv = 1.0f;
 }
 
 }  // namespace
 
-hipError_t launch_empty_scale(float* scale, float* scale_inv, hipStream_t st) {
-  empty_scale_kernel<<<1, 1, 0, st>>>(scale, scale_inv);
+hipError_t launch_empty_scale(float* amax, float* scale, float* scale_inv, hipStream_t st) {
+  empty_scale_kernel<<<1, 1, 0, st>>>(amax, scale, scale_inv);
   return hipGetLastError();
 }
 

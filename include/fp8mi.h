@@ -79,7 +79,8 @@ extern "C" {
 
 /* quantize recipes [P1 sec. 2.1-2.3] */
 #define FP8MI_TENSOR_CURRENT 0 /* amax of x now -> s; writes amax, scale, scale_inv    */
-#define FP8MI_TENSOR_DELAYED 1 /* cast with *scale; max-accumulates amax of x into *amax */
+#define FP8MI_TENSOR_DELAYED 1 /* cast with *scale; max-accumulates max|x| into the     */
+                               /* amax accumulator float[FP8MI_AMAX_SLOTS]             */
 #define FP8MI_BLOCK_1x128 2    /* ROW: 1x128 along cols; COL: 128x1 down rows            */
 #define FP8MI_BLOCK_128x128 3  /* one scale per 128x128 tile                             */
 #define FP8MI_MX_1x32 4        /* ROW: 1x32 along cols; COL: 32x1 down rows; E8M0 bytes  */
@@ -94,6 +95,13 @@ extern "C" {
 #define FP8MI_GEMM_BLOCK_1x128_128x128 1 /* s_a [M x ceil(K/128)], s_b [ceil(N/128) x ceil(K/128)] */
 #define FP8MI_GEMM_BLOCK_1x128_1x128 2   /* s_a [M x ceil(K/128)], s_b [N x ceil(K/128)]      */
 #define FP8MI_GEMM_MX_1x32 3             /* s_a [M x ceil(K/32)], s_b [N x ceil(K/32)] E8M0   */
+
+/* Slots of a delayed-scaling amax accumulator.  Each workgroup of a
+ * TENSOR_DELAYED cast max-accumulates into a slot of its own with plain
+ * loads and stores; fp8_amax_history_update folds the slots into the step's
+ * amax.  (Atomics on one address serialise on MI355X; with a thousand
+ * workgroups they would cost as much as the cast itself.) */
+#define FP8MI_AMAX_SLOTS 1024
 
 /* ---- entry points ----------------------------------------------------- */
 
@@ -120,13 +128,20 @@ extern "C" {
  *        TENSOR_*      same scale as ROW (a plain transpose of the codes).
  *   scale, scale_inv, amax       : per-tensor recipes only (device floats).
  *        CURRENT: writes amax = max|x| (NaN if x holds a NaN), scale and
- *                 scale_inv.
- *        DELAYED: reads *scale; *amax = max(*amax, max|x|) -- the caller
- *                 zeroes it once, fp8_amax_history_update consumes and
- *                 re-zeroes it; scale_inv is not touched.
+ *                 scale_inv.  Before the cast, the first code output (q_row,
+ *                 else q_col) briefly holds per-workgroup partial maxima
+ *                 inside its [rows x cols] (resp. [cols x rows]) bytes.
+ *        DELAYED: reads *scale; amax is the accumulator
+ *                 float[FP8MI_AMAX_SLOTS]: the step's amax is the largest
+ *                 slot (NaN-dominant, comparing |x| bit patterns) and a cast
+ *                 raises slots to cover max|x| of x.  The caller zeroes it
+ *                 once; fp8_amax_history_update consumes and re-zeroes it.
+ *                 Casts that share an accumulator must be ordered on one
+ *                 stream.  scale_inv is not touched.
  *   nonfinite                    : optional (may be NULL) device int32; gets
  *        += the number of scale blocks whose amax was NaN/Inf (CURRENT and
  *        block recipes; those blocks use s = 1, MX byte 0xFF).
+ * x must not overlap any output.
  * Alignment: x, q_row, q_col 16-byte aligned; ld_x * sizeof(elem),
  * ld_q_row and ld_q_col multiples of 16 bytes.  rows == 0 or cols == 0 is
  * allowed (CURRENT then writes amax = 0, scale = scale_inv = 1).
@@ -143,10 +158,10 @@ int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t
  *  the maximum of the buffer; P2 sec. 3.3: interval 1 = every step, margin]
  *
  *   history  : float [len] ring, zero-initialised by the caller; head: int32.
- *   amax     : float, the amax accumulated since the previous update (as
- *              written by fp8_quantize with TENSOR_DELAYED); read, then
- *              reset to 0.
- *   If *amax is finite it is written to history[*head] and
+ *   amax     : float[FP8MI_AMAX_SLOTS], the accumulator that fp8_quantize
+ *              with TENSOR_DELAYED filled since the previous update; its
+ *              largest slot is the step's amax a; every slot is reset to 0.
+ *   If a is finite it is written to history[*head] and
  *   head = (head + 1) % len; otherwise *nonfinite += 1 and nothing is
  *   pushed.  Then scale = s(max(history)), scale_inv = fl32(1 / scale).
  *   len in [1, 65536]; margin in [0, 64].  One workgroup; device state only. */

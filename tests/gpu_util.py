@@ -40,6 +40,13 @@ def same_f32(a, b) -> bool:
     return bool(np.array_equal(na, nb) and np.array_equal(f32_bits(a)[~na], f32_bits(b)[~nb]))
 
 
+def acc_amax(acc: torch.Tensor) -> np.float32:
+    """The amax a delayed-scaling accumulator holds: its largest slot, compared
+    as |x| bit patterns so that a NaN slot wins."""
+    bits = host(acc).view(np.uint32)
+    return np.uint32(bits.max()).view(np.float32)
+
+
 def parallel_encode(fmt: str, v: np.ndarray) -> np.ndarray:
     """oracle.encode over a large array, split across threads (ctypes drops the GIL)."""
     oracle.encode(fmt, np.zeros(1, np.float32))  # build the oracle's table once

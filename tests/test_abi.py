@@ -33,8 +33,18 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (fp8_\w+)$", out, flags=re.M))
     assert set(_declared()) <= exported
-    assert fm.version() == 100
+    assert fm.version() == 200
     assert fm.status_string(fm.ERR_ALIGN).startswith("pointer")
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"^#define FP8MI_(\w+) \(?(-?\d+)\)?", text, flags=re.M))
+    assert len(defs) >= 25
+    for name, val in defs.items():
+        assert getattr(fm, name) == int(val), name
+    launch = open(os.path.join(ROOT, "fp8_scaled_quantization_scale_amd", "csrc", "launch.hpp")).read()
+    assert int(re.search(r"kAmaxSlots = (\d+);", launch).group(1)) == int(defs["AMAX_SLOTS"])
 
 
 def _q(**kw):

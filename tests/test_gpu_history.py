@@ -10,7 +10,7 @@ import torch
 import fp8_scaled_quantization_scale_amd as fm
 import oracle
 import workloads
-from gpu_util import host, need_gpu, same_f32
+from gpu_util import acc_amax, host, need_gpu, same_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -21,8 +21,10 @@ def _run(state: fm.DelayedState, ref: oracle.History, draws, check_every=1):
         oq, am = oracle.quantize_delayed(ref.fmt, x.float().cpu().numpy(), ref.scale)
         if t % check_every == 0:
             assert np.array_equal(host(q.q_row)[:, : x.shape[1]], oq), t
-            assert same_f32(host(state.amax), [am]), t
+            assert same_f32([acc_amax(state.amax)], [am]), t
         state.update()
+        if t % check_every == 0:
+            assert not host(state.amax).view(np.uint32).any(), t
         ref.update(am)
         if t % check_every == 0:
             assert same_f32(host(state.scale), [ref.scale]), t

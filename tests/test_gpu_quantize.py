@@ -10,7 +10,7 @@ import torch
 import fp8_scaled_quantization_scale_amd as fm
 import oracle
 import workloads
-from gpu_util import FMT_NAME, codes, dev, host, need_gpu, parallel_encode, same_f32
+from gpu_util import FMT_NAME, acc_amax, codes, dev, host, need_gpu, parallel_encode, same_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,7 @@ def test_tensor_delayed_matches_oracle(fmt, dtype):
     need_gpu()
     scale = np.float32(300.0 if fmt == fm.E4M3 else 4.0e4)
     acc = np.float32(0.0)
-    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(fm.AMAX_SLOTS, dtype=torch.float32, device="cuda")
     s_dev = torch.tensor([scale], device="cuda")
     for si, (rows, cols) in enumerate(SHAPES):
         x = _input(rows, cols, 300 + si, dtype, specials=si == 0)
@@ -96,7 +96,7 @@ def test_tensor_delayed_matches_oracle(fmt, dtype):
         acc = max(acc, am)
         assert np.array_equal(codes(q.q_row, rows, cols), oq)
         assert np.array_equal(codes(q.q_col, cols, rows), oq.T)
-        assert same_f32(host(amax), [acc])
+        assert same_f32([acc_amax(amax)], [acc])
 
 
 @pytest.mark.parametrize("recipe", [fm.TENSOR_CURRENT, fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32])
@@ -145,6 +145,71 @@ def test_empty_current_writes_unit_scale(fmt):
     assert host(q.amax)[0] == 0.0 and host(q.scale)[0] == 1.0 and host(q.scale_inv)[0] == 1.0
 
 
+@pytest.mark.parametrize("orient", [fm.ROW, fm.COL, fm.ROW_AND_COL])
+@pytest.mark.parametrize("shape", [(1000, 3), (3, 1000), (2, 2), (4100, 4), (2048, 1536)])
+def test_tensor_current_thin_and_padded(orient, shape):
+    """Current scaling on thin shapes (fewer than 4 output bytes per row, a
+    single reduction workgroup) and on a tensor large enough for many partial
+    maxima, with padded code outputs: the padding bytes are never written."""
+    need_gpu()
+    rows, cols = shape
+    ld_x = cols + (-cols) % 8  # 16-byte rows; the padding holds data that must not count
+    xfull = _input(rows, ld_x, 250 + rows + cols, torch.bfloat16, specials=True)
+    xfull[:, cols:] *= 1000.0
+    x = xfull[:, :cols]
+    ld_r, ld_c = cols + 48 - cols % 16, rows + 48 - rows % 16
+    q_row = torch.full((rows, ld_r), 0xAB, dtype=torch.uint8, device="cuda")
+    q_col = torch.full((cols, ld_c), 0xCD, dtype=torch.uint8, device="cuda")
+    f = lambda: torch.zeros(1, dtype=torch.float32, device="cuda")  # noqa: E731
+    sc, si, am = f(), f(), f()
+    st = fm.fp8_quantize(xfull.cuda(), fm.IN_BF16, rows, cols, ld_x, fm.TENSOR_CURRENT, fm.E4M3, orient, 0,
+                         q_row, ld_r, None, q_col, ld_c, None, sc, si, am, None)
+    assert st == fm.OK
+    oq, s, s_inv, a, _ = oracle.quantize_current("e4m3", x.float().numpy())
+    assert same_f32(host(am), [a]) and same_f32(host(sc), [s]) and same_f32(host(si), [s_inv])
+    qr, qc = host(q_row), host(q_col)
+    if orient & fm.ROW:
+        assert np.array_equal(qr[:, :cols], oq)
+    else:
+        assert (qr == 0xAB).all()
+    if orient & fm.COL:
+        assert np.array_equal(qc[:, :rows], oq.T)
+    else:
+        assert (qc == 0xCD).all()
+    assert (qr[:, cols:] == 0xAB).all() and (qc[:, rows:] == 0xCD).all()
+
+
+def test_tensor_current_strided_input():
+    """ld_x larger than cols with current scaling (the 2-D amax pass)."""
+    need_gpu()
+    base = _input(700, 1280, 510, torch.bfloat16)
+    base[650, 1100] = 1e4  # outside the view: must not count
+    base[10, 900] = -30.0
+    xv = base.cuda()[:, :1000]
+    q = fm.quantize(xv, fm.TENSOR_CURRENT, fm.E4M3, fm.ROW_AND_COL)
+    oq, s, s_inv, a, _ = oracle.quantize_current("e4m3", base[:, :1000].float().numpy())
+    assert same_f32(host(q.amax), [a]) and same_f32(host(q.scale), [s])
+    assert np.array_equal(codes(q.q_row, 700, 1000), oq)
+    assert np.array_equal(codes(q.q_col, 1000, 700), oq.T)
+
+
+def test_delayed_accumulator_slots():
+    """A delayed cast only raises slots; slots it does not own keep their
+    value, and a larger value already in a slot survives."""
+    need_gpu()
+    x = _input(512, 1024, 520, torch.bfloat16).cuda()
+    amax = torch.zeros(fm.AMAX_SLOTS, dtype=torch.float32, device="cuda")
+    amax[fm.AMAX_SLOTS - 1] = 7.0e6
+    amax[0] = 123.0
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    fm.quantize(x, fm.TENSOR_DELAYED, fm.E5M2, fm.ROW, scale=one, amax=amax)
+    _, am = oracle.quantize_delayed("e5m2", x.float().cpu().numpy(), np.float32(1.0))
+    h = host(amax)
+    # the grid is far smaller than the slot count, so the last slot is not this cast's
+    assert h[-1] == np.float32(7.0e6) and h[0] >= np.float32(123.0)
+    assert h[:-1].max() == max(np.float32(123.0), am)
+
+
 def test_strided_input_rows():
     """ld_x larger than cols: only the first cols elements of each row count."""
     need_gpu()
@@ -180,7 +245,7 @@ def test_every_fp32_input_safe_path(fmt):
     need_gpu()
     name = FMT_NAME[fmt]
     one = torch.ones(1, dtype=torch.float32, device="cuda")
-    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(fm.AMAX_SLOTS, dtype=torch.float32, device="cuda")
     bad = 0
     for start in range(0, 1 << 32, CHUNK):
         bits = np.arange(start, start + CHUNK, dtype=np.uint64).astype(np.uint32)

@@ -137,9 +137,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   const int lr = lane & 15;  // fragment row
   const int lg = lane >> 4;  // lane group
 
-  // ---- tile assignment: XCD-contiguous ranges of the grid, grouped along M
-  int pid = blockIdx.x;
+  // ---- persistent: the workgroup walks tiles blockIdx.x, blockIdx.x +
+  // gridDim.x, ... (tiles t and t + gridDim.x stay on one XCD when
+  // gridDim.x % 8 == 0); one tile's output stores drain while the next
+  // tile's loads and MFMAs run
   const int total = p.tiles_m * p.tiles_n;
+#pragma unroll 1
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  __syncthreads();  // every wave is done with the previous tile's LDS stages
+  // ---- tile assignment: XCD-contiguous ranges of the tile index, grouped along M
+  int pid = tile;
   if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
   constexpr int GROUP_M = 8;
   const int in_group = GROUP_M * p.tiles_n;
@@ -197,25 +204,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
     rsb = make_rsrc(reinterpret_cast<const uint8_t*>(p.sb) + (int64_t)n0 * nkb, (uint32_t)(rows_b * nkb));
   }
 
+  // A words come first and fill whole waves, so each wave reads one matrix's
+  // scales through one (scalar) buffer resource
+  static_assert(SA_W % 64 == 0, "A scale words end on a wave boundary");
   auto load_scales = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < SLW; ++i) {
       const int t = tid + NTHR * i;
-      const bool isa = t < SA_W;
+      const bool isa = 64 * wave + NTHR * i < SA_W;  // wave-uniform
       const int r = isa ? t : t - SA_W;  // row (or 128-row tile) within the panel
+      const __amdgpu_buffer_rsrc_t rsrc = isa ? rsa : rsb;
       if constexpr (kBlock) {
         const uint32_t off = (t < S_W) ? (uint32_t)((r * nkb + kt) * 4) : kOOB;
-        rs[i] = isa ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0)
-                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsb, off, 0, 0);
+        rs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
       } else if constexpr (REC == kGemmMx) {
         uint32_t w = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kb = 4 * kt + j;
           const uint32_t off = (t < S_W && kb < nkb) ? (uint32_t)(r * nkb + kb) : kOOB;
-          const uint32_t byte = isa ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0)
-                                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsb, off, 0, 0);
-          w |= byte << (8 * j);
+          w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, off, 0, 0) << (8 * j);
         }
         rs[i] = w;
       }
@@ -406,6 +414,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       }
     }
   }
+  }  // tile loop
 }
 
 // Tile configuration per recipe (measured on MI355X): workgroup tile BM x BN
@@ -416,6 +425,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 //           fits two waves per SIMD, so one wave's FMAs overlap the other's MFMAs;
 //   MX      256x256, 4 waves of 128x128: the scale operands push 128x64 waves
 //           past 256 registers, so one wave per SIMD with the full register file.
+// compute units of the current device (queried once per process and device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int REC>
 struct TileCfg {
   static constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
@@ -446,7 +468,10 @@ hipError_t launch4(const GemmParams& g, hipStream_t st) {
   a.c = g.c;
   a.tiles_m = (int)((g.M + BM - 1) / BM);
   a.tiles_n = (int)((g.N + BN - 1) / BN);
-  const unsigned blocks = (unsigned)a.tiles_m * (unsigned)a.tiles_n;
+  // persistent grid: one workgroup per compute unit (the LDS ring admits one)
+  const unsigned tiles = (unsigned)a.tiles_m * (unsigned)a.tiles_n;
+  const unsigned cus = (unsigned)cu_count();
+  const unsigned blocks = tiles < cus ? tiles : cus;
   gemm_kernel<FA, FB, REC, OUT, BM, BN, WAVES_M, WAVES_N, STAGES>
       <<<blocks, 64 * WAVES_M * WAVES_N, 0, st>>>(a);
   return hipGetLastError();

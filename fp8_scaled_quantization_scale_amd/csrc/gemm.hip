@@ -31,6 +31,8 @@
 //   MX          E8M0 scales fed to the scaled MFMA (no VALU work);
 //   BLOCK_*     each 128-deep K block is an MFMA into a zeroed FP32 partial,
 //               then acc += (s_a[row, kb] * s_b[.., kb]) * partial on the VALU.
+#include <utility>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -51,9 +53,19 @@ __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
-template <int FA, int FB>
-__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+// MX tile step: acc[i][j] += B-fragment j x A-fragment i (the C^T form) with
+// E8M0 scales.  Lane scale words hold one byte per sub-tile: A sub-tile i in
+// byte i % 4 of sa[i / 4], B sub-tile j in byte j % 4 of sb[j / 4]; op_sel
+// picks the byte, so the pack is expanded at compile time.
+// (sub-tile pairs OFF + IJ, i-major)
+template <int FA, int FB, int MT, int NT, int OFF, int... IJ>
+__device__ __forceinline__ void mx_mfmas(std::integer_sequence<int, IJ...>, v4f (&acc)[MT][NT], const v8i (&fa)[MT],
+                                         const v8i (&fb)[NT], const uint32_t* sa, const uint32_t* sb) {
+  ((acc[(OFF + IJ) / NT][(OFF + IJ) % NT] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        fb[(OFF + IJ) % NT], fa[(OFF + IJ) / NT], acc[(OFF + IJ) / NT][(OFF + IJ) % NT], FB, FA,
+        ((OFF + IJ) % NT) % 4, (int)sb[((OFF + IJ) % NT) / 4], ((OFF + IJ) / NT) % 4,
+        (int)sa[((OFF + IJ) / NT) / 4])),
+   ...);
 }
 
 // LDS chunk swizzles (16-byte chunk c of tile row r lives at slot c ^ swz(r)).
@@ -127,7 +139,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t sscale[STAGES][S_W > 0 ? S_W : 1];
+  constexpr bool kMx = REC == kGemmMx;
+  // block recipes: FP32 scale words of a K step (A rows, then B rows / tiles)
+  __shared__ __attribute__((aligned(16))) uint32_t sscale[STAGES][(S_W > 0 && !kMx) ? S_W : 1];
+  // MX: E8M0 bytes of a K step by K block g: A at [g * BM + pos_a], B at
+  // [4 BM + g * BN + pos_b], ordered so that a lane's sub-tile scales are
+  // consecutive (see mx_pos_a / mx_pos_b)
+  __shared__ __attribute__((aligned(16))) uint8_t sbytes[STAGES][kMx ? 4 * (BM + BN) : 1];
 
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   const int tid = threadIdx.x;
@@ -218,22 +236,56 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
         const uint32_t off = (t < S_W) ? (uint32_t)((r * nkb + kt) * 4) : kOOB;
         rs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
       } else if constexpr (REC == kGemmMx) {
-        uint32_t w = 0;
+        if ((nkb & 3) == 0) {  // the step's 4 bytes are one aligned dword
+          const uint32_t off = (t < S_W) ? (uint32_t)(r * nkb + 4 * kt) : kOOB;
+          rs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+        } else {
+          uint32_t w = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kb = 4 * kt + j;
-          const uint32_t off = (t < S_W && kb < nkb) ? (uint32_t)(r * nkb + kb) : kOOB;
-          w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, off, 0, 0) << (8 * j);
+          for (int j = 0; j < 4; ++j) {
+            const int kb = 4 * kt + j;
+            const uint32_t off = (t < S_W && kb < nkb) ? (uint32_t)(r * nkb + kb) : kOOB;
+            w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, off, 0, 0) << (8 * j);
+          }
+          rs[i] = w;
         }
-        rs[i] = w;
       }
     }
+  };
+  // MX byte positions: A row r = wm WM + 16 i + lr goes to wm WM + lr MT + i;
+  // B row r = wn WN + brow(j) (lr = 4 (w / CPL) + w % 4, j = (w % CPL) / 4
+  // with w = r % WN) goes to wn WN + lr NT + j
+  auto mx_pos_a = [&](int r) {
+    const int w = r % WM;
+    return (r - w) + (w % 16) * MT + w / 16;
+  };
+  auto mx_pos_b = [&](int r) {
+    constexpr int CPLB = 4 * NT;
+    const int w = r % WN;
+    return (r - w) + (4 * (w / CPLB) + w % 4) * NT + (w % CPLB) / 4;
   };
   auto store_scales = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < SLW; ++i) {
       const int t = tid + NTHR * i;
-      if (t < S_W) sscale[kt % STAGES][t] = rs[i];
+      if constexpr (kMx) {
+        const bool isa = 64 * wave + NTHR * i < SA_W;  // wave-uniform
+        if (t < S_W) {
+          uint8_t* dst = sbytes[kt % STAGES];
+          const uint32_t w = rs[i];
+          if (isa) {
+            const int pos = mx_pos_a(t);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) dst[g * BM + pos] = (uint8_t)(w >> (8 * g));
+          } else {
+            const int pos = mx_pos_b(t - SA_W);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) dst[4 * BM + g * BN + pos] = (uint8_t)(w >> (8 * g));
+          }
+        }
+      } else {
+        if (t < S_W) sscale[kt % STAGES][t] = rs[i];
+      }
     }
   };
 
@@ -294,10 +346,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
     const uint8_t* la = smem + st * TILE_BYTES;
     const uint8_t* lb = la + BM * kBK;
     v8i fa[MT], fb[NT];
+    if constexpr (!kMx) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int row = wm * WM + i * 16 + lr;
-      fa[i] = frag(la, row, swz_a(row));
+      for (int i = 0; i < MT; ++i) {
+        const int row = wm * WM + i * 16 + lr;
+        fa[i] = frag(la, row, swz_a(row));
+      }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -313,15 +367,32 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
     } else if constexpr (REC == kGemmMx) {
-      int sa[MT], sb[NT];
+      // lane group lg supplies K block lg: its MT A bytes and NT B bytes
+      static_assert(MT % 4 == 0 && NT % 4 == 0, "whole scale words per lane");
+      uint32_t sa[MT / 4], sb[NT / 4];
+      const uint8_t* sbase = sbytes[st];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) sa[i] = (int)((sscale[st][wm * WM + i * 16 + lr] >> (8 * lg)) & 0xFFu);
+      for (int q = 0; q < MT / 4; ++q)
+        sa[q] = *reinterpret_cast<const uint32_t*>(sbase + lg * BM + wm * WM + lr * MT + 4 * q);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sb[j] = (int)((sscale[st][SA_W + wn * WN + brow(j)] >> (8 * lg)) & 0xFFu);
+      for (int q = 0; q < NT / 4; ++q)
+        sb[q] = *reinterpret_cast<const uint32_t*>(sbase + 4 * BM + lg * BN + wn * WN + lr * NT + 4 * q);
+      // two halves of the A fragments, kept apart by scheduling barriers so
+      // that only half of them are live at a time
+      auto load_fa = [&](int i0, int i1) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma_mx<FB, FA>(fb[j], fa[i], acc[i][j], sb[j], sa[i]);
+        for (int i = i0; i < i1; ++i) {
+          const int row = wm * WM + i * 16 + lr;
+          fa[i] = frag(la, row, swz_a(row));
+        }
+      };
+      load_fa(0, MT / 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_mfmas<FA, FB, MT, NT, 0>(std::make_integer_sequence<int, MT / 2 * NT>{}, acc, fa, fb, sa, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_fa(MT / 2, MT);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_mfmas<FA, FB, MT, NT, MT / 2 * NT>(std::make_integer_sequence<int, MT / 2 * NT>{}, acc, fa, fb, sa, sb);
     } else {
       // the A scale of this lane's row in each M sub-tile
       float sa[MT];
@@ -423,8 +494,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 //           two waves per SIMD hide each other's LDS waits;
 //   block   256x128, 8 waves of 64x64: the VGPR accumulator of the promotion
 //           fits two waves per SIMD, so one wave's FMAs overlap the other's MFMAs;
-//   MX      256x256, 4 waves of 128x128: the scale operands push 128x64 waves
-//           past 256 registers, so one wave per SIMD with the full register file.
+//   MX      256x256, 8 waves of 128x64 like tensor: a lane's E8M0 scales for
+//           a K step fit three registers (op_sel picks the byte).
 // compute units of the current device (queried once per process and device)
 int cu_count() {
   static int cached[64] = {0};
@@ -444,7 +515,7 @@ struct TileCfg {
   static constexpr int BM = 256;
   static constexpr int BN = kBlock ? 128 : 256;
   static constexpr int WAVES_M = kBlock ? 4 : 2;
-  static constexpr int WAVES_N = REC == kGemmTensor ? 4 : 2;
+  static constexpr int WAVES_N = kBlock ? 2 : 4;
 };
 
 template <int FA, int FB, int REC, int OUT>

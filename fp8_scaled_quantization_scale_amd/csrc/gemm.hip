@@ -140,8 +140,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * TILE_BYTES];
   constexpr bool kMx = REC == kGemmMx;
-  // block recipes: FP32 scale words of a K step (A rows, then B rows / tiles)
-  __shared__ __attribute__((aligned(16))) uint32_t sscale[STAGES][(S_W > 0 && !kMx) ? S_W : 1];
+  // block recipes: FP32 scale words of a K step (A rows, then B rows / tiles;
+  // every thread stores a word, zeros past S_W)
+  constexpr int SLW = S_W > 0 ? (S_W + NTHR - 1) / NTHR : 0;  // scale words per thread
+  __shared__ __attribute__((aligned(16))) uint32_t sscale[STAGES][(S_W > 0 && !kMx) ? SLW * NTHR : 1];
   // MX: E8M0 bytes of a K step by K block g: A at [g * BM + pos_a], B at
   // [4 BM + g * BN + pos_b], ordered so that a lane's sub-tile scales are
   // consecutive (see mx_pos_a / mx_pos_b)
@@ -203,7 +205,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   // ---- scales: fetched with range-checked buffer loads (zero past the matrix)
   // into VGPRs before a step's tile DMAs, written to LDS at the end of the
   // iteration; every lane issues the same count so vmcnt stays uniform
-  constexpr int SLW = S_W > 0 ? (S_W + NTHR - 1) / NTHR : 0;  // scale words per thread
   uint32_t rs[SLW > 0 ? SLW : 1];
   __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
   int nkb = 0;
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
           }
         }
       } else {
-        if (t < S_W) sscale[kt % STAGES][t] = rs[i];
+        sscale[kt % STAGES][t] = rs[i];  // branch-free: keeps the K step one scheduling region
       }
     }
   };
@@ -398,22 +399,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       float sa[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) sa[i] = __builtin_bit_cast(float, sscale[st][wm * WM + i * 16 + lr]);
+      // Per-element scale of sub-tile (i, j), column r: 128x128 B tiles give
+      // one B scale for the whole wave, 1x128 B blocks one per column.
+      float sb[NT][4];
       if constexpr (REC == kGemmBlock128x128) {
         static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie inside one 128-wide B tile");
         const float sbv = __builtin_bit_cast(float, sscale[st][SA_W + (wn * WN) / 128]);
 #pragma unroll
         for (int i = 0; i < MT; ++i) sa[i] *= sbv;
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const v4f part = mfma<FB, FA>(fb[j], fa[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[i], acc[i][j][r]);
-          }
       } else {
         // B scales of this lane's 4 NT columns (lg*CPL .. +CPL), 4 per sub-tile
-        float sb[NT][4];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           const uint4 w = *reinterpret_cast<const uint4*>(&sscale[st][SA_W + wn * WN + lg * CPL + 4 * j]);
@@ -422,17 +417,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
           sb[j][2] = __builtin_bit_cast(float, w.z);
           sb[j][3] = __builtin_bit_cast(float, w.w);
         }
+      }
+      // Software pipeline: each 128-deep block product goes to a zeroed
+      // partial, and the promotion acc += s * partial of sub-tile k - LAG is
+      // issued right after the MFMA of sub-tile k, so the FMAs run while the
+      // matrix core works (a ring of LAG + 1 partials; the scheduling barriers
+      // keep the compiler from regrouping all MFMAs ahead of all FMAs).
+      constexpr int NSUB = MT * NT, LAG = 4;
+      v4f part[LAG + 1];
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+      for (int k = 0; k < NSUB + LAG; ++k) {
+        if (k < NSUB) part[k % (LAG + 1)] = mfma<FB, FA>(fb[k % NT], fa[k / NT], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        if (k >= LAG) {
+          const int q = k - LAG, i = q / NT, j = q % NT;
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const v4f part = mfma<FB, FA>(fb[j], fa[i], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[i] * sb[j][r], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) {
+            const float sc = (REC == kGemmBlock128x128) ? sa[i] : sa[i] * sb[j][r];
+            acc[i][j][r] = __builtin_fmaf(part[q % (LAG + 1)][r], sc, acc[i][j][r]);
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if constexpr (S_W > 0)
+    // (block recipes store unconditionally: after the last step the stage
+    // written is one no wave reads before the next tile refills it)
+    if constexpr (kBlock)
+      store_scales(kt + STAGES - 1);
+    else if constexpr (S_W > 0)
       if (kt + STAGES - 1 < KT) store_scales(kt + STAGES - 1);
   }
 

@@ -124,13 +124,16 @@ class Step:
             _ok(fm.fp8_gemm_scaled(self.qg, fm.E5M2, st.scale_inv, N, self.qwt, fm.E4M3, self.siw, N,
                                    fm.GEMM_TENSOR, M, K, N, self.dx, fm.OUT_BF16, K))
 
+        # the history update closes the step: dgrad must dequantize G's codes
+        # with the scale_inv they were cast with, and the update replaces it
+        # by the next step's
         self.ops = [
             ("quant_x_current_e4m3", "quant", M * K * 3, qx),
             ("quant_w_current_e4m3_row_col", "quant", N * K * 4, qw),
             ("quant_g_delayed_e5m2", "quant", M * N * 3, qg),
-            ("history_update", "small", 0, hist),
             ("gemm_fprop", "gemm", 2 * M * N * K, fprop),
             ("gemm_dgrad", "gemm", 2 * M * N * K, dgrad),
+            ("history_update", "small", 0, hist),
         ]
 
     def _build_block(self):

@@ -1,0 +1,198 @@
+"""GPU parity at the bench workloads' full sizes, in the launch configuration
+bench.py times (its Step, one input copy, one step).
+
+Quantization: codes and scales bit for bit on sampled rows, sampled columns
+of the transposed layouts and sampled 128x128 tile rows / columns; per-tensor
+amax, scales and the delayed-scaling history step checked on whole tensors.
+GEMMs: every entry of two corner 128x128 output tiles and of a cross of ~66
+random rows x ~66 random columns, within |C - C_ref| <= 2^-10 S + 2^-8 |C_ref|
+(BF16 output), C_ref and S from the oracle in float64 on the GPU's own codes
+and scales (per-tensor scales from the oracle's own amax)."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import fp8_scaled_quantization_scale_amd as fm
+import oracle
+import workloads
+from gpu_util import host, need_gpu, same_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def pick(n: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    idx = {0, n - 1} | set(rng.choice(n, size=min(k, n), replace=False).tolist())
+    return np.array(sorted(idx))
+
+
+def _ix(t: torch.Tensor, idx) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(idx), device=t.device)
+
+
+def rows_f32(t, idx) -> np.ndarray:
+    return t[_ix(t, idx)].float().cpu().numpy()
+
+
+def cols_f32(t, idx) -> np.ndarray:
+    """Columns idx of t as rows: [len(idx) x t.rows]."""
+    return np.ascontiguousarray(t[:, _ix(t, idx)].float().cpu().numpy().T)
+
+
+def rows_u8(t, idx, n) -> np.ndarray:
+    return t[_ix(t, idx)][:, :n].cpu().numpy()
+
+
+def rows_np(t, idx) -> np.ndarray:
+    return t[_ix(t, idx)].cpu().numpy()
+
+
+def check_gemm(c, deq_a, deq_b, M, N, tag):
+    """c [M x N] BF16 against the oracle; deq_a(idx) / deq_b(idx) give float64
+    dequantized operand rows (contraction index last)."""
+    I, J = pick(M, 64, 11), pick(N, 64, 12)
+    cref, s = oracle.gemm_ref(deq_a(I), deq_b(J))
+    got = c[_ix(c, I)][:, _ix(c, J)].float().cpu().numpy()
+    bad = oracle.gemm_violations(got, cref, s, "bf16")
+    assert not bad.any(), (tag, "cross", int(bad.sum()))
+    for r0, c0 in ((0, 0), (M - 128, N - 128)):
+        ri, cj = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+        cref, s = oracle.gemm_ref(deq_a(ri), deq_b(cj))
+        got = c[r0:r0 + 128, c0:c0 + 128].float().cpu().numpy()
+        bad = oracle.gemm_violations(got, cref, s, "bf16")
+        assert not bad.any(), (tag, "tile", r0, c0, int(bad.sum()))
+
+
+def check_rows_blocks(x, q, s, idx, br, bc, mx, tag):
+    """ROW-layout codes / scales of sampled rows (1 x bc blocks)."""
+    xf = rows_f32(x, idx)
+    oq, og, _ = (oracle.quantize_mx if mx else oracle.quantize_blocks)("e4m3", xf, br, bc)
+    assert np.array_equal(rows_u8(q, idx, x.shape[1]), oq), (tag, "codes")
+    assert np.array_equal(rows_np(s, idx), og), (tag, "scales")
+
+
+def check_cols_blocks(x, qt, st, idx, mx, tag):
+    """COL-layout codes / scales of sampled columns (blocks down each column)."""
+    xt = cols_f32(x, idx)
+    bc = 32 if mx else 128
+    oq, og, _ = (oracle.quantize_mx if mx else oracle.quantize_blocks)("e4m3", xt, 1, bc)
+    assert np.array_equal(rows_u8(qt, idx, x.shape[0]), oq), (tag, "codes")
+    assert np.array_equal(rows_np(st, idx), og), (tag, "scales")
+
+
+def check_tiles(w, q, s, qt, st, tile_rows, tile_cols, tag):
+    """128x128 recipe: whole tile rows (ROW layout) and tile columns (COL)."""
+    N, K = w.shape
+    for t in tile_rows:
+        rr = np.arange(128 * t, min(128 * t + 128, N))
+        oq, og, _ = oracle.quantize_blocks("e4m3", rows_f32(w, rr), 128, 128)
+        assert np.array_equal(rows_u8(q, rr, K), oq), (tag, "row tile", t)
+        assert np.array_equal(host(s[t]), og[0]), (tag, "row tile scales", t)
+    for u in tile_cols:
+        cc = np.arange(128 * u, min(128 * u + 128, K))
+        oq, og, _ = oracle.quantize_blocks("e4m3", cols_f32(w, cc), 128, 128)
+        assert np.array_equal(rows_u8(qt, cc, N), oq), (tag, "col tile", u)
+        assert np.array_equal(host(st[u]), og[0]), (tag, "col tile scales", u)
+
+
+def _step(name):
+    need_gpu()
+    torch.cuda.empty_cache()
+    cfg = workloads.CONFIGS[name]
+    return cfg, bench.Step(cfg, 1)
+
+
+def test_fullsize_tensor_llama3_8b_attn():
+    cfg, st = _step("llama3_8b_attn_tensor")
+    M, N, K = cfg.M, cfg.N, cfg.K
+    ds = st.state
+    s_pre, si_pre = host(ds.scale)[0], host(ds.scale_inv)[0]
+    ring_pre, head_pre = host(ds.history).copy(), int(host(ds.head)[0])
+    assert si_pre == np.float32(1.0) / s_pre  # state holds the pair the cast uses
+    st.run(0)
+    torch.cuda.synchronize()
+    X, W, G = st.X[0], st.W[0], st.G[0]
+
+    # current scaling of X and W: whole-tensor amax and scales, sampled codes
+    scales = {}
+    for name, t, q, s, si, am, qt in (("X", X, st.qx, st.sx, st.six, st.ax, None),
+                                      ("W", W, st.qw, st.sw, st.siw, st.aw, st.qwt)):
+        a = oracle.amax(t.float().cpu().numpy())
+        os_, osi, _ = oracle.scale_from_amax("e4m3", a)
+        assert same_f32(host(am), [a]) and same_f32(host(s), [os_]) and same_f32(host(si), [osi]), name
+        scales[name] = (os_, osi)
+        r = pick(t.shape[0], 24, 3)
+        oq, _ = oracle.quantize_delayed("e4m3", rows_f32(t, r), os_)
+        assert np.array_equal(rows_u8(q, r, t.shape[1]), oq), name
+        if qt is not None:
+            c = pick(t.shape[1], 24, 4)
+            oq, _ = oracle.quantize_delayed("e4m3", cols_f32(t, c), os_)
+            assert np.array_equal(rows_u8(qt, c, t.shape[0]), oq), name + "^T"
+
+    # delayed scaling of G with the scale carried in, then the history step
+    r = pick(M, 24, 5)
+    oq, _ = oracle.quantize_delayed("e5m2", rows_f32(G, r), s_pre)
+    assert np.array_equal(rows_u8(st.qg, r, N), oq)
+    a_g = oracle.amax(G.float().cpu().numpy())
+    ring = ring_pre.copy()
+    ring[head_pre] = a_g
+    assert np.array_equal(host(ds.history), ring)
+    assert int(host(ds.head)[0]) == (head_pre + 1) % 200
+    s_new, si_new, _ = oracle.scale_from_amax("e5m2", ring.max())
+    assert same_f32(host(ds.scale), [s_new]) and same_f32(host(ds.scale_inv), [si_new])
+    assert not host(ds.amax).view(np.uint32).any()
+
+    # GEMMs: fprop with the oracle's scales; dgrad with the scale_inv G was cast with
+    sx_inv, sw_inv = scales["X"][1], scales["W"][1]
+    check_gemm(st.y, lambda i: oracle.dequant("e4m3", rows_u8(st.qx, i, K), sx_inv),
+               lambda j: oracle.dequant("e4m3", rows_u8(st.qw, j, K), sw_inv), M, N, "fprop")
+    check_gemm(st.dx, lambda i: oracle.dequant("e5m2", rows_u8(st.qg, i, N), si_pre),
+               lambda j: oracle.dequant("e4m3", rows_u8(st.qwt, j, N), sw_inv), M, K, "dgrad")
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_mlp_block", "llama31_405b_mlp_block"])
+def test_fullsize_block(name):
+    cfg, st = _step(name)
+    M, N, K = cfg.M, cfg.N, cfg.K
+    st.run(0)
+    torch.cuda.synchronize()
+    X, W, G = st.X[0], st.W[0], st.G[0]
+
+    check_rows_blocks(X, st.qx, st.sx, pick(M, 24, 3), 1, 128, False, "X")
+    check_cols_blocks(X, st.qxt, st.sxt, pick(K, 24, 4), False, "X^T")
+    check_rows_blocks(G, st.qg, st.sg, pick(M, 24, 5), 1, 128, False, "G")
+    check_cols_blocks(G, st.qgt, st.sgt, pick(N, 24, 6), False, "G^T")
+    tn, tk = N // 128, K // 128
+    check_tiles(W, st.qw, st.sw, st.qwt, st.swt, [0, tn // 2, tn - 1], [0, tk // 2, tk - 1], "W")
+
+    def deq_1x128(q, s, n):
+        return lambda i: oracle.dequant("e4m3", rows_u8(q, i, n), rows_np(s, i), 1, 128)
+
+    def deq_tiles(q, s, n):  # rows of a 128x128-tiled operand: scale row = tile row
+        return lambda j: oracle.dequant("e4m3", rows_u8(q, j, n), rows_np(s, np.asarray(j) // 128), 1, 128)
+
+    check_gemm(st.y, deq_1x128(st.qx, st.sx, K), deq_tiles(st.qw, st.sw, K), M, N, "fprop")
+    check_gemm(st.dx, deq_1x128(st.qg, st.sg, N), deq_tiles(st.qwt, st.swt, N), M, K, "dgrad")
+    check_gemm(st.dw, deq_1x128(st.qgt, st.sgt, M), deq_1x128(st.qxt, st.sxt, M), N, K, "wgrad")
+
+
+def test_fullsize_mx_llama3_70b_mlp():
+    cfg, st = _step("llama3_70b_mlp_mx")
+    M, N, K = cfg.M, cfg.N, cfg.K
+    st.run(0)
+    torch.cuda.synchronize()
+    X, W, G = st.X[0], st.W[0], st.G[0]
+
+    for name, t, q, s, qt, sT, rows, cols in (("X", X, st.qx, st.sx, st.qxt, st.sxt, M, K),
+                                              ("W", W, st.qw, st.sw, st.qwt, st.swt, N, K),
+                                              ("G", G, st.qg, st.sg, st.qgt, st.sgt, M, N)):
+        check_rows_blocks(t, q, s, pick(rows, 24, 7), 1, 32, True, name)
+        check_cols_blocks(t, qt, sT, pick(cols, 24, 8), True, name + "^T")
+
+    def deq(q, s, n):
+        return lambda i: oracle.dequant_mx("e4m3", rows_u8(q, i, n), rows_np(s, i), 1, 32)
+
+    check_gemm(st.y, deq(st.qx, st.sx, K), deq(st.qw, st.sw, K), M, N, "fprop")
+    check_gemm(st.dx, deq(st.qg, st.sg, N), deq(st.qwt, st.swt, N), M, K, "dgrad")
+    check_gemm(st.dw, deq(st.qgt, st.sgt, M), deq(st.qxt, st.sxt, M), N, K, "wgrad")

@@ -123,6 +123,23 @@ struct ScaleTraits {
   }
 };
 
+// Tile configuration per recipe (measured on MI355X): workgroup tile BM x BN
+// with WAVES_M x WAVES_N waves.
+//   tensor  256x256, 8 waves of 128x64: accumulator inside the matrix core,
+//           two waves per SIMD hide each other's LDS waits;
+//   block   256x128, 8 waves of 64x64: the VGPR accumulator of the promotion
+//           fits two waves per SIMD, so one wave's FMAs overlap the other's MFMAs;
+//   MX      256x256, 8 waves of 128x64 like tensor: a lane's E8M0 scales for
+//           a K step fit three registers (op_sel picks the byte).
+template <int REC>
+struct TileCfg {
+  static constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
+  static constexpr int BM = 256;
+  static constexpr int BN = kBlock ? 128 : 256;
+  static constexpr int WAVES_M = kBlock ? 4 : 2;
+  static constexpr int WAVES_N = kBlock ? 2 : 4;
+};
+
 template <int FA, int FB, int REC, int OUT, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p) {
   constexpr int NTHR = 64 * WAVES_M * WAVES_N;
@@ -325,6 +342,78 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // ---- one K step, split into reading its operands (LDS -> registers) and
+  // computing on them, so that the two can run in different phases
+  v8i fa[MT], fb[NT];
+  float bsa[kBlock ? MT : 1];         // block recipes: A row scales (x the B tile scale)
+  float bsb[kBlock ? NT : 1][4];      // block 1x128 B: per-column scales
+  auto load_step = [&](int kt) {
+    const int st = kt % STAGES;
+    const uint8_t* la = smem + st * TILE_BYTES;
+    const uint8_t* lb = la + BM * kBK;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = wm * WM + i * 16 + lr;
+      fa[i] = frag(la, row, swz_a(row));
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int row = wn * WN + brow(j);
+      fb[j] = frag(lb, row, swz_b(row));
+    }
+    if constexpr (kBlock) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) bsa[i] = __builtin_bit_cast(float, sscale[st][wm * WM + i * 16 + lr]);
+      if constexpr (REC == kGemmBlock128x128) {
+        static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie inside one 128-wide B tile");
+        const float sbv = __builtin_bit_cast(float, sscale[st][SA_W + (wn * WN) / 128]);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) bsa[i] *= sbv;
+      } else {
+        // B scales of this lane's 4 NT columns (lg*CPL .. +CPL), 4 per sub-tile
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const uint4 w = *reinterpret_cast<const uint4*>(&sscale[st][SA_W + wn * WN + lg * CPL + 4 * j]);
+          bsb[j][0] = __builtin_bit_cast(float, w.x);
+          bsb[j][1] = __builtin_bit_cast(float, w.y);
+          bsb[j][2] = __builtin_bit_cast(float, w.z);
+          bsb[j][3] = __builtin_bit_cast(float, w.w);
+        }
+      }
+    }
+  };
+  // The MFMA computes C^T tiles (B fragment first): lane (lr, lg) then holds
+  // row i*16 + lr and columns lg*CPL + 4j + r of the wave tile.
+  auto compute = [&]() {
+    if constexpr (REC == kGemmTensor) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
+    } else if constexpr (kBlock) {
+      // Software pipeline: each 128-deep block product goes to a zeroed
+      // partial, and the promotion acc += s * partial of sub-tile k - LAG is
+      // issued right after the MFMA of sub-tile k, so the FMAs run while the
+      // matrix core works (a ring of LAG + 1 partials; the scheduling barriers
+      // keep the compiler from regrouping all MFMAs ahead of all FMAs).
+      constexpr int NSUB = MT * NT, LAG = 4;
+      v4f part[LAG + 1];
+#pragma unroll
+      for (int k = 0; k < NSUB + LAG; ++k) {
+        if (k < NSUB) part[k % (LAG + 1)] = mfma<FB, FA>(fb[k % NT], fa[k / NT], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        if (k >= LAG) {
+          const int q = k - LAG, i = q / NT, j = q % NT;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sc = (REC == kGemmBlock128x128) ? bsa[i] : bsa[i] * bsb[j][r];
+            acc[i][j][r] = __builtin_fmaf(part[q % (LAG + 1)][r], sc, acc[i][j][r]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // prologue: STAGES - 1 steps in flight
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -344,30 +433,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
     if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
 
     const int st = kt % STAGES;
-    const uint8_t* la = smem + st * TILE_BYTES;
-    const uint8_t* lb = la + BM * kBK;
-    v8i fa[MT], fb[NT];
-    if constexpr (!kMx) {
+    if constexpr (REC == kGemmMx) {
+      const uint8_t* la = smem + st * TILE_BYTES;
+      const uint8_t* lb = la + BM * kBK;
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int row = wm * WM + i * 16 + lr;
-        fa[i] = frag(la, row, swz_a(row));
+      for (int j = 0; j < NT; ++j) {
+        const int row = wn * WN + brow(j);
+        fb[j] = frag(lb, row, swz_b(row));
       }
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int row = wn * WN + brow(j);
-      fb[j] = frag(lb, row, swz_b(row));
-    }
-
-    // The MFMA computes C^T tiles (B fragment first): lane (lr, lg) then holds
-    // row i*16 + lr and columns lg*CPL + 4j + r of the wave tile.
-    if constexpr (REC == kGemmTensor) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
-    } else if constexpr (REC == kGemmMx) {
       // lane group lg supplies K block lg: its MT A bytes and NT B bytes
       static_assert(MT % 4 == 0 && NT % 4 == 0, "whole scale words per lane");
       uint32_t sa[MT / 4], sb[NT / 4];
@@ -395,49 +468,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       __builtin_amdgcn_sched_barrier(0);
       mx_mfmas<FA, FB, MT, NT, MT / 2 * NT>(std::make_integer_sequence<int, MT / 2 * NT>{}, acc, fa, fb, sa, sb);
     } else {
-      // the A scale of this lane's row in each M sub-tile
-      float sa[MT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) sa[i] = __builtin_bit_cast(float, sscale[st][wm * WM + i * 16 + lr]);
-      // Per-element scale of sub-tile (i, j), column r: 128x128 B tiles give
-      // one B scale for the whole wave, 1x128 B blocks one per column.
-      float sb[NT][4];
-      if constexpr (REC == kGemmBlock128x128) {
-        static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie inside one 128-wide B tile");
-        const float sbv = __builtin_bit_cast(float, sscale[st][SA_W + (wn * WN) / 128]);
-#pragma unroll
-        for (int i = 0; i < MT; ++i) sa[i] *= sbv;
-      } else {
-        // B scales of this lane's 4 NT columns (lg*CPL .. +CPL), 4 per sub-tile
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const uint4 w = *reinterpret_cast<const uint4*>(&sscale[st][SA_W + wn * WN + lg * CPL + 4 * j]);
-          sb[j][0] = __builtin_bit_cast(float, w.x);
-          sb[j][1] = __builtin_bit_cast(float, w.y);
-          sb[j][2] = __builtin_bit_cast(float, w.z);
-          sb[j][3] = __builtin_bit_cast(float, w.w);
-        }
-      }
-      // Software pipeline: each 128-deep block product goes to a zeroed
-      // partial, and the promotion acc += s * partial of sub-tile k - LAG is
-      // issued right after the MFMA of sub-tile k, so the FMAs run while the
-      // matrix core works (a ring of LAG + 1 partials; the scheduling barriers
-      // keep the compiler from regrouping all MFMAs ahead of all FMAs).
-      constexpr int NSUB = MT * NT, LAG = 4;
-      v4f part[LAG + 1];
-#pragma unroll
-      for (int k = 0; k < NSUB + LAG; ++k) {
-        if (k < NSUB) part[k % (LAG + 1)] = mfma<FB, FA>(fb[k % NT], fa[k / NT], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-        if (k >= LAG) {
-          const int q = k - LAG, i = q / NT, j = q % NT;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sc = (REC == kGemmBlock128x128) ? sa[i] : sa[i] * sb[j][r];
-            acc[i][j][r] = __builtin_fmaf(part[q % (LAG + 1)][r], sc, acc[i][j][r]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      load_step(kt);
+      compute();
     }
     // (block recipes store unconditionally: after the last step the stage
     // written is one no wave reads before the next tile refills it)
@@ -499,14 +531,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   }  // tile loop
 }
 
-// Tile configuration per recipe (measured on MI355X): workgroup tile BM x BN
-// with WAVES_M x WAVES_N waves.
-//   tensor  256x256, 8 waves of 128x64: accumulator inside the matrix core,
-//           two waves per SIMD hide each other's LDS waits;
-//   block   256x128, 8 waves of 64x64: the VGPR accumulator of the promotion
-//           fits two waves per SIMD, so one wave's FMAs overlap the other's MFMAs;
-//   MX      256x256, 8 waves of 128x64 like tensor: a lane's E8M0 scales for
-//           a K step fit three registers (op_sel picks the byte).
 // compute units of the current device (queried once per process and device)
 int cu_count() {
   static int cached[64] = {0};
@@ -520,14 +544,7 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int REC>
-struct TileCfg {
-  static constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
-  static constexpr int BM = 256;
-  static constexpr int BN = kBlock ? 128 : 256;
-  static constexpr int WAVES_M = kBlock ? 4 : 2;
-  static constexpr int WAVES_N = kBlock ? 2 : 4;
-};
+
 
 template <int FA, int FB, int REC, int OUT>
 hipError_t launch4(const GemmParams& g, hipStream_t st) {

@@ -17,37 +17,50 @@ namespace fp8mi {
 
 namespace {
 
+constexpr int kHistThreads = 1024;
+
+// One round of loads (a slot and a ring entry per thread), one reduction.
+// The ring maximum leaves out entry h, which the step's amax replaces when
+// it is pushed and which is folded back in when it is not.
 template <int FMT>
-__global__ __launch_bounds__(256) void history_kernel(float* ring, int32_t* head, int len, float* amax,
-                                                      int margin, float* scale, float* scale_inv,
-                                                      int32_t* nonfinite) {
-  __shared__ uint32_t redk[4];
-  __shared__ float red[4];
-  // the step's amax: NaN-dominant max over the slots (|x| bit patterns)
+__global__ __launch_bounds__(kHistThreads) void history_kernel(float* ring, int32_t* head, int len, float* amax,
+                                                               int margin, float* scale, float* scale_inv,
+                                                               int32_t* nonfinite) {
+  __shared__ uint32_t redk[kHistThreads / 64];
+  __shared__ float redr[kHistThreads / 64];
   uint32_t* slots = reinterpret_cast<uint32_t*>(amax);
+  const int t = threadIdx.x;
+  const int h = *head;
+  // the step's amax: NaN-dominant max over the slots (|x| bit patterns)
   uint32_t k = 0;
-  for (int i = threadIdx.x; i < kAmaxSlots; i += blockDim.x) {
+  for (int i = t; i < kAmaxSlots; i += kHistThreads) {
     const uint32_t v = slots[i];
     k = k > v ? k : v;
   }
+  float m = 0.0f;  // ring entries are finite and non-negative
+  for (int i = t; i < len; i += kHistThreads)
+    if (i != h) m = fmaxf(m, ring[i]);
   k = group_max_u32<64>(k);
-  if ((threadIdx.x & 63) == 0) redk[threadIdx.x >> 6] = k;
-  const int h = *head;
-  __syncthreads();  // every slot and *head have been read before they are rewritten
-  const uint32_t k01 = redk[0] > redk[1] ? redk[0] : redk[1];
-  const uint32_t k23 = redk[2] > redk[3] ? redk[2] : redk[3];
-  const float a = key_to_float(k01 > k23 ? k01 : k23);
-  const bool push = is_finite(a);
-  float m = push ? a : 0.0f;  // the pushed value replaces ring[h]
-  for (int i = threadIdx.x; i < len; i += blockDim.x)
-    if (!(push && i == h)) m = fmaxf(m, ring[i]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  for (int i = threadIdx.x; i < kAmaxSlots; i += blockDim.x) slots[i] = 0u;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if ((t & 63) == 0) {
+    redk[t >> 6] = k;
+    redr[t >> 6] = m;
+  }
+  const float ring_h = ring[h];
+  __syncthreads();  // every slot and ring entry has been read before they are rewritten
+  for (int i = t; i < kAmaxSlots; i += kHistThreads) slots[i] = 0u;
+  if (t == 0) {
+    k = 0;
+    m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kHistThreads / 64; ++w) {
+      k = k > redk[w] ? k : redk[w];
+      m = fmaxf(m, redr[w]);
+    }
+    const float a = key_to_float(k);
+    const bool push = is_finite(a);
+    m = fmaxf(m, push ? a : ring_h);
     if (push) {
       ring[h] = a;
       *head = (h + 1) % len;
@@ -65,9 +78,9 @@ __global__ __launch_bounds__(256) void history_kernel(float* ring, int32_t* head
 hipError_t launch_history(float* history, int32_t* head, int len, float* amax, int fmt, int margin,
                           float* scale, float* scale_inv, int32_t* nonfinite, hipStream_t st) {
   if (fmt == kE4M3)
-    history_kernel<kE4M3><<<1, 256, 0, st>>>(history, head, len, amax, margin, scale, scale_inv, nonfinite);
+    history_kernel<kE4M3><<<1, kHistThreads, 0, st>>>(history, head, len, amax, margin, scale, scale_inv, nonfinite);
   else
-    history_kernel<kE5M2><<<1, 256, 0, st>>>(history, head, len, amax, margin, scale, scale_inv, nonfinite);
+    history_kernel<kE5M2><<<1, kHistThreads, 0, st>>>(history, head, len, amax, margin, scale, scale_inv, nonfinite);
   return hipGetLastError();
 }
 

@@ -123,21 +123,19 @@ struct ScaleTraits {
   }
 };
 
-// Tile configuration per recipe (measured on MI355X): workgroup tile BM x BN
-// with WAVES_M x WAVES_N waves.
-//   tensor  256x256, 8 waves of 128x64: accumulator inside the matrix core,
-//           two waves per SIMD hide each other's LDS waits;
-//   block   256x128, 8 waves of 64x64: the VGPR accumulator of the promotion
-//           fits two waves per SIMD, so one wave's FMAs overlap the other's MFMAs;
-//   MX      256x256, 8 waves of 128x64 like tensor: a lane's E8M0 scales for
-//           a K step fit three registers (op_sel picks the byte).
+// Tile configuration (measured on MI355X): every recipe runs 256x256
+// workgroup tiles with 8 waves of 128x64, two waves per SIMD hiding each
+// other's LDS waits.  The block recipes fit it because their A fragments are
+// read one M sub-tile ahead inside the promotion pipeline (two live instead
+// of eight); MX because a lane's E8M0 scales for a K step fit three
+// registers (op_sel picks the byte).  256x128 tiles cost the block recipes
+// 11-32% (more LDS and DMA traffic per flop).
 template <int REC>
 struct TileCfg {
-  static constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
   static constexpr int BM = 256;
-  static constexpr int BN = kBlock ? 128 : 256;
-  static constexpr int WAVES_M = kBlock ? 4 : 2;
-  static constexpr int WAVES_N = kBlock ? 2 : 4;
+  static constexpr int BN = 256;
+  static constexpr int WAVES_M = 2;
+  static constexpr int WAVES_N = 4;
 };
 
 template <int FA, int FB, int REC, int OUT, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
@@ -347,14 +345,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   v8i fa[MT], fb[NT];
   float bsa[kBlock ? MT : 1];         // block recipes: A row scales (x the B tile scale)
   float bsb[kBlock ? NT : 1][4];      // block 1x128 B: per-column scales
+  const uint8_t* la_cur = smem;  // A tile of the step being computed
+  auto load_fa = [&](int i) {
+    const int row = wm * WM + i * 16 + lr;
+    fa[i] = frag(la_cur, row, swz_a(row));
+  };
   auto load_step = [&](int kt) {
     const int st = kt % STAGES;
     const uint8_t* la = smem + st * TILE_BYTES;
     const uint8_t* lb = la + BM * kBK;
+    la_cur = la;
+    if constexpr (!kBlock) {  // block recipes load A progressively in compute()
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int row = wm * WM + i * 16 + lr;
-      fa[i] = frag(la, row, swz_a(row));
+      for (int i = 0; i < MT; ++i) load_fa(i);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -395,11 +398,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       // partial, and the promotion acc += s * partial of sub-tile k - LAG is
       // issued right after the MFMA of sub-tile k, so the FMAs run while the
       // matrix core works (a ring of LAG + 1 partials; the scheduling barriers
-      // keep the compiler from regrouping all MFMAs ahead of all FMAs).
+      // keep the compiler from regrouping all MFMAs ahead of all FMAs).  A
+      // fragments are read one M sub-tile ahead, so two are live at a time.
       constexpr int NSUB = MT * NT, LAG = 4;
       v4f part[LAG + 1];
+      load_fa(0);
 #pragma unroll
       for (int k = 0; k < NSUB + LAG; ++k) {
+        if (k < NSUB && k % NT == 0 && k / NT + 1 < MT) load_fa(k / NT + 1);
         if (k < NSUB) part[k % (LAG + 1)] = mfma<FB, FA>(fb[k % NT], fa[k / NT], v4f{0.0f, 0.0f, 0.0f, 0.0f});
         if (k >= LAG) {
           const int q = k - LAG, i = q / NT, j = q % NT;

@@ -57,14 +57,24 @@ __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
 // E8M0 scales.  Lane scale words hold one byte per sub-tile: A sub-tile i in
 // byte i % 4 of sa[i / 4], B sub-tile j in byte j % 4 of sb[j / 4]; op_sel
 // picks the byte, so the pack is expanded at compile time.
-// (sub-tile pairs OFF + IJ, i-major)
-template <int FA, int FB, int MT, int NT, int OFF, int... IJ>
-__device__ __forceinline__ void mx_mfmas(std::integer_sequence<int, IJ...>, v4f (&acc)[MT][NT], const v8i (&fa)[MT],
-                                         const v8i (&fb)[NT], const uint32_t* sa, const uint32_t* sb) {
-  ((acc[(OFF + IJ) / NT][(OFF + IJ) % NT] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-        fb[(OFF + IJ) % NT], fa[(OFF + IJ) / NT], acc[(OFF + IJ) / NT][(OFF + IJ) % NT], FB, FA,
-        ((OFF + IJ) % NT) % 4, (int)sb[((OFF + IJ) % NT) / 4], ((OFF + IJ) / NT) % 4,
-        (int)sa[((OFF + IJ) / NT) / 4])),
+// (one M sub-tile I against all NT B sub-tiles)
+template <int FA, int FB, int MT, int NT, int I, int... J>
+__device__ __forceinline__ void mx_row(std::integer_sequence<int, J...>, v4f (&acc)[MT][NT], const v8i& fa,
+                                       const v8i (&fb)[NT], const uint32_t* sa, const uint32_t* sb) {
+  ((acc[I][J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[J], fa, acc[I][J], FB, FA, J % 4,
+                                                                  (int)sb[J / 4], I % 4, (int)sa[I / 4])),
+   ...);
+}
+// All M sub-tiles in order; the A fragment of sub-tile I + 1 is read while
+// sub-tile I computes (load_fa), and each sub-tile is its own scheduling
+// region, so two A fragments are live at a time.
+template <int FA, int FB, int MT, int NT, class LoadFa, int... I>
+__device__ __forceinline__ void mx_rows(std::integer_sequence<int, I...>, LoadFa&& load_fa, v4f (&acc)[MT][NT],
+                                        const v8i (&fa)[MT], const v8i (&fb)[NT], const uint32_t* sa,
+                                        const uint32_t* sb) {
+  ((load_fa(I + 1 < MT ? I + 1 : -1),
+    mx_row<FA, FB, MT, NT, I>(std::make_integer_sequence<int, NT>{}, acc, fa[I], fb, sa, sb),
+    __builtin_amdgcn_sched_barrier(0)),
    ...);
 }
 
@@ -285,20 +295,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
     for (int i = 0; i < SLW; ++i) {
       const int t = tid + NTHR * i;
       if constexpr (kMx) {
+        // branch-free (every thread owns a row), so the K step stays one
+        // scheduling region
+        static_assert(S_W == SLW * NTHR, "one scale row per thread");
         const bool isa = 64 * wave + NTHR * i < SA_W;  // wave-uniform
-        if (t < S_W) {
-          uint8_t* dst = sbytes[kt % STAGES];
-          const uint32_t w = rs[i];
-          if (isa) {
-            const int pos = mx_pos_a(t);
+        const int base = isa ? mx_pos_a(t) : 4 * BM + mx_pos_b(t - SA_W);
+        const int gstride = isa ? BM : BN;
+        uint8_t* dst = sbytes[kt % STAGES] + base;
+        const uint32_t w = rs[i];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) dst[g * BM + pos] = (uint8_t)(w >> (8 * g));
-          } else {
-            const int pos = mx_pos_b(t - SA_W);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) dst[4 * BM + g * BN + pos] = (uint8_t)(w >> (8 * g));
-          }
-        }
+        for (int g = 0; g < 4; ++g) dst[g * gstride] = (uint8_t)(w >> (8 * g));
       } else {
         sscale[kt % STAGES][t] = rs[i];  // branch-free: keeps the K step one scheduling region
       }
@@ -457,32 +463,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
 #pragma unroll
       for (int q = 0; q < NT / 4; ++q)
         sb[q] = *reinterpret_cast<const uint32_t*>(sbase + 4 * BM + lg * BN + wn * WN + lr * NT + 4 * q);
-      // two halves of the A fragments, kept apart by scheduling barriers so
-      // that only half of them are live at a time
-      auto load_fa = [&](int i0, int i1) {
-#pragma unroll
-        for (int i = i0; i < i1; ++i) {
-          const int row = wm * WM + i * 16 + lr;
-          fa[i] = frag(la, row, swz_a(row));
-        }
+      auto load_fa_mx = [&](int i) {
+        if (i < 0) return;
+        const int row = wm * WM + i * 16 + lr;
+        fa[i] = frag(la, row, swz_a(row));
       };
-      load_fa(0, MT / 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mx_mfmas<FA, FB, MT, NT, 0>(std::make_integer_sequence<int, MT / 2 * NT>{}, acc, fa, fb, sa, sb);
-      __builtin_amdgcn_sched_barrier(0);
-      load_fa(MT / 2, MT);
-      __builtin_amdgcn_sched_barrier(0);
-      mx_mfmas<FA, FB, MT, NT, MT / 2 * NT>(std::make_integer_sequence<int, MT / 2 * NT>{}, acc, fa, fb, sa, sb);
+      load_fa_mx(0);
+      mx_rows<FA, FB, MT, NT>(std::make_integer_sequence<int, MT>{}, load_fa_mx, acc, fa, fb, sa, sb);
     } else {
       load_step(kt);
       compute();
     }
-    // (block recipes store unconditionally: after the last step the stage
-    // written is one no wave reads before the next tile refills it)
-    if constexpr (kBlock)
-      store_scales(kt + STAGES - 1);
-    else if constexpr (S_W > 0)
-      if (kt + STAGES - 1 < KT) store_scales(kt + STAGES - 1);
+    // (stored unconditionally: after the last step the stage written is one
+    // no wave reads before the next tile refills it)
+    if constexpr (S_W > 0) store_scales(kt + STAGES - 1);
   }
 
   // ---- epilogue: each lane writes CPL consecutive columns of its rows with

@@ -360,11 +360,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
     const int st = kt % STAGES;
     const uint8_t* la = smem + st * TILE_BYTES;
     const uint8_t* lb = la + BM * kBK;
-    la_cur = la;
-    if constexpr (!kBlock) {  // block recipes load A progressively in compute()
-#pragma unroll
-      for (int i = 0; i < MT; ++i) load_fa(i);
-    }
+    la_cur = la;  // A fragments are read in compute(), one M sub-tile ahead of use
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int row = wn * WN + brow(j);
@@ -395,10 +391,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   // row i*16 + lr and columns lg*CPL + 4j + r of the wave tile.
   auto compute = [&]() {
     if constexpr (REC == kGemmTensor) {
+      // A fragment i + 1 is read while sub-tile row i computes; one
+      // scheduling region per row keeps two A fragments live
+      load_fa(0);
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) {
+        if (i + 1 < MT) load_fa(i + 1);
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else if constexpr (kBlock) {
       // Software pipeline: each 128-deep block product goes to a zeroed
       // partial, and the promotion acc += s * partial of sub-tile k - LAG is

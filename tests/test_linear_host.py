@@ -1,0 +1,73 @@
+"""Host logic of the FP8 linear layer: recipe -> library calls, the autocast
+stack, argument checks, and that there is no path other than the GPU one."""
+import pytest
+import torch
+
+import fp8_scaled_quantization_scale_amd as fm
+from fp8_scaled_quantization_scale_amd import linear as fl
+
+
+def test_plan_per_recipe():
+    p = fl.plan(fl.DelayedScaling())
+    assert p.quant == {"x": (fm.TENSOR_DELAYED, fm.E4M3), "w": (fm.TENSOR_DELAYED, fm.E4M3),
+                       "g": (fm.TENSOR_DELAYED, fm.E5M2)}
+    assert set(p.gemm.values()) == {fm.GEMM_TENSOR}
+    p = fl.plan(fl.Float8CurrentScaling(fp8_format=fl.Format.E4M3, margin=2))
+    assert p.quant["g"] == (fm.TENSOR_CURRENT, fm.E4M3) and p.margin == 2
+    p = fl.plan(fl.DelayedScaling(fp8_format=fl.Format.E5M2))
+    assert {f for _, f in p.quant.values()} == {fm.E5M2}
+    p = fl.plan(fl.Float8BlockScaling())
+    assert p.quant == {"x": (fm.BLOCK_1x128, fm.E4M3), "w": (fm.BLOCK_128x128, fm.E4M3),
+                       "g": (fm.BLOCK_1x128, fm.E4M3)}
+    assert p.gemm == {"fprop": fm.GEMM_BLOCK_1x128_128x128, "dgrad": fm.GEMM_BLOCK_1x128_128x128,
+                      "wgrad": fm.GEMM_BLOCK_1x128_1x128}
+    p = fl.plan(fl.MXFP8BlockScaling(fp8_format=fl.Format.HYBRID))
+    assert p.quant["x"] == (fm.MX_1x32, fm.E4M3) and p.quant["g"] == (fm.MX_1x32, fm.E5M2)
+    assert set(p.gemm.values()) == {fm.GEMM_MX_1x32}
+
+
+@pytest.mark.parametrize("bad", [None, "delayed", fl.DelayedScaling(interval=0),
+                                 fl.DelayedScaling(amax_history_len=0),
+                                 fl.Float8CurrentScaling(margin=65)])
+def test_bad_recipes_rejected(bad):
+    with pytest.raises(fm.Fp8Error):
+        fl.plan(bad)
+
+
+def test_autocast_stack():
+    assert fl.active_recipe() is None
+    a, b = fl.Float8BlockScaling(), fl.Float8CurrentScaling()
+    with fl.fp8_autocast(fp8_recipe=a):
+        assert fl.active_recipe() is a
+        with fl.fp8_autocast(fp8_recipe=b):
+            assert fl.active_recipe() is b
+            with fl.fp8_autocast(enabled=False):
+                assert fl.active_recipe() is b
+        assert fl.active_recipe() is a
+    assert fl.active_recipe() is None
+    with fl.fp8_autocast():
+        assert isinstance(fl.active_recipe(), fl.DelayedScaling)
+    with pytest.raises(fm.Fp8Error):
+        with fl.fp8_autocast(fp8_recipe="mx"):
+            pass
+    assert fl.active_recipe() is None
+
+
+def test_constructor_checks():
+    with pytest.raises(fm.Fp8Error):
+        fl.Linear(64, 64, bias=True)
+    with pytest.raises(fm.Fp8Error):
+        fl.Linear(60, 64)
+    with pytest.raises(fm.Fp8Error):
+        fl.Linear(64, 40)
+    lin = fl.Linear(64, 32)
+    assert lin.weight.shape == (32, 64) and lin.weight.dtype == torch.bfloat16
+
+
+def test_no_path_but_the_gpu():
+    lin = fl.Linear(64, 32, recipe=fl.Float8CurrentScaling())
+    x = torch.randn(16, 64, dtype=torch.bfloat16)
+    with pytest.raises(fm.Fp8Error, match="GPU"):
+        lin(x)
+    with pytest.raises(fm.Fp8Error, match="recipe"):
+        fl.Linear(64, 32)(x)

@@ -406,6 +406,68 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
 
 
+# ---------------------------------------------------------------------------
+# FP8-vs-BF16 GEMM speedup over K ("Mastering FP8 LLM training", Fig. 1)
+# ---------------------------------------------------------------------------
+
+SWEEP_K = (1024, 2048, 4096, 8192, 16384)
+
+
+def _time_ms(fn, reps: int, ev: HipEvents) -> float:
+    """Median over 3 blocks of `reps` back-to-back launches (fence-free events)."""
+    fn()
+    torch.cuda.synchronize()
+    blocks = []
+    for _ in range(3):
+        ev.record(0, False)
+        for _ in range(reps):
+            fn()
+        ev.record(0, True)
+        torch.cuda.synchronize()
+        blocks.append(ev.ms(0) / reps)
+    return float(np.median(blocks))
+
+
+def speedup_sweep(M: int, N: int, ks, reps: int):
+    """One JSON line per K: TFLOP/s of the BF16 GEMM (same kernel, BF16
+    matrix-core instruction) and of the scaled FP8 GEMM in each scaling
+    recipe, and each recipe's speedup over BF16.  Operands: N(0, 1) BF16
+    A [M x K], N(0, 0.02) B [N x K], quantized by the library with the
+    recipe's own granularity (rows of A 1x128 / 1x32, B per recipe).
+    hipBLASLt's BF16 GEMM (torch.matmul) is timed beside it for context."""
+    ev = HipEvents(1)
+    recipes = (("tensor", fm.TENSOR_CURRENT, fm.TENSOR_CURRENT, fm.GEMM_TENSOR),
+               ("1x128_128x128", fm.BLOCK_1x128, fm.BLOCK_128x128, fm.GEMM_BLOCK_1x128_128x128),
+               ("1x128_1x128", fm.BLOCK_1x128, fm.BLOCK_1x128, fm.GEMM_BLOCK_1x128_1x128),
+               ("mx_1x32", fm.MX_1x32, fm.MX_1x32, fm.GEMM_MX_1x32))
+    for K in ks:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4242 + K)
+        a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        b = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        flop = 2.0 * M * N * K
+        c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        line = {"sweep": "fp8_vs_bf16_gemm", "M": M, "N": N, "K": K, "out": "bf16"}
+        t_bf = _time_ms(lambda: fm.bf16_gemm(a, b, c=c), reps, ev)
+        line["bf16"] = {"ms": round(t_bf, 4), "tflops": round(flop / t_bf / 1e9, 1)}
+        bt = b.t().contiguous()  # [K x N]; a plain 2-D product, no transposed view
+        t_lt = _time_ms(lambda: torch.mm(a, bt, out=c), reps, ev)
+        line["bf16_hipblaslt"] = {"ms": round(t_lt, 4), "tflops": round(flop / t_lt / 1e9, 1)}
+        for name, ra, rb, rg in recipes:
+            qa = fm.quantize(a, ra, fm.E4M3, fm.ROW)
+            qb = fm.quantize(b, rb, fm.E4M3, fm.ROW)
+            sa = qa.scale_inv if rg == fm.GEMM_TENSOR else qa.s_row
+            sb = qb.scale_inv if rg == fm.GEMM_TENSOR else qb.s_row
+            t = _time_ms(lambda: fm.gemm(qa.q_row, fm.E4M3, sa, qb.q_row, fm.E4M3, sb, rg, K,
+                                         M=M, N=N, c=c), reps, ev)
+            line[name] = {"ms": round(t, 4), "tflops": round(flop / t / 1e9, 1),
+                          "speedup_vs_bf16": round(t_bf / t, 3)}
+            del qa, qb
+        print(json.dumps(line), flush=True)
+        del a, b, c
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,7 +478,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (reference for the HBM byte counters)")
+    ap.add_argument("--speedup-sweep", action="store_true",
+                    help="only print the FP8-vs-BF16 GEMM speedup over K (one JSON line per K)")
+    ap.add_argument("--sweep-mn", type=int, default=8192, help="M = N of the speedup sweep")
     args = ap.parse_args()
+    if args.speedup_sweep:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        speedup_sweep(args.sweep_mn, args.sweep_mn, SWEEP_K, 10)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return

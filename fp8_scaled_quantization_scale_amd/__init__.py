@@ -36,7 +36,7 @@ AMAX_SLOTS = 1024  # floats in a delayed-scaling amax accumulator
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
 TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
 
-EXPORTS = ("fp8_quantize", "fp8_amax_history_update", "fp8_gemm_scaled",
+EXPORTS = ("fp8_quantize", "fp8_amax_history_update", "fp8_gemm_scaled", "fp8_bf16_gemm",
            "fp8_status_string", "fp8_version")
 
 
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH):
     lib.fp8_gemm_scaled.restype = i32
     lib.fp8_gemm_scaled.argtypes = [vp, i32, vp, i64, vp, i32, vp, i64, i32, i64, i64, i64,
                                     vp, i32, i64, vp]
+    lib.fp8_bf16_gemm.restype = i32
+    lib.fp8_bf16_gemm.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i32, i64, vp]
     lib.fp8_status_string.restype = ctypes.c_char_p
     lib.fp8_status_string.argtypes = [i32]
     lib.fp8_version.restype = i32
@@ -124,6 +126,10 @@ def fp8_gemm_scaled(a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, M, N, K, c, 
                     stream=None) -> int:
     return load().fp8_gemm_scaled(_p(a), fmt_a, _p(s_a), lda, _p(b), fmt_b, _p(s_b), ldb, recipe,
                                   M, N, K, _p(c), c_dtype, ldc, _stream(stream))
+
+
+def fp8_bf16_gemm(a, lda, b, ldb, M, N, K, c, c_dtype, ldc, stream=None) -> int:
+    return load().fp8_bf16_gemm(_p(a), lda, _p(b), ldb, M, N, K, _p(c), c_dtype, ldc, _stream(stream))
 
 
 # ---------------------------------------------------------------------------
@@ -216,6 +222,20 @@ def gemm(a: torch.Tensor, fmt_a: int, s_a: torch.Tensor, b: torch.Tensor, fmt_b:
     st = fp8_gemm_scaled(a, fmt_a, s_a, a.stride(0), b, fmt_b, s_b, b.stride(0), recipe,
                          M, N, K, c, c_dtype, c.stride(0), stream)
     _check(st, "fp8_gemm_scaled")
+    return c
+
+
+def bf16_gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16,
+              c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C[M x N] = a[M x K] . b[N x K]^T, BF16 operands (row-major, unit column stride)."""
+    assert a.dtype == b.dtype == torch.bfloat16 and a.stride(1) == 1 and b.stride(1) == 1
+    M, K = a.shape
+    N = b.shape[0]
+    if c is None:
+        c = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    c_dtype = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_FP32
+    _check(fp8_bf16_gemm(a, a.stride(0), b, b.stride(0), M, N, K, c, c_dtype, c.stride(0), stream),
+           "fp8_bf16_gemm")
     return c
 
 

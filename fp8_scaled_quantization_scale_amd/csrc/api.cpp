@@ -114,6 +114,26 @@ int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, c
   return hip_status(fp8mi::launch_gemm(p, (hipStream_t)stream));
 }
 
+int fp8_bf16_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                  void* c, int c_dtype, int64_t ldc, void* stream) {
+  if (c_dtype != FP8MI_OUT_BF16 && c_dtype != FP8MI_OUT_FP32) return FP8MI_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0) return FP8MI_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8MI_OK;
+  if (!c) return FP8MI_ERR_NULL;
+  if (ldc < N) return FP8MI_ERR_SHAPE;
+  if (K > 0) {
+    if (!a || !b) return FP8MI_ERR_NULL;
+    if (K % 8) return FP8MI_ERR_SHAPE;
+    if (lda < K || ldb < K) return FP8MI_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || lda % 8 || ldb % 8) return FP8MI_ERR_ALIGN;
+  }
+  if (M > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x3FFFFFFFLL) return FP8MI_ERR_UNSUPPORTED;
+  if (K > 0 && (lda > (1LL << 21) || ldb > (1LL << 21))) return FP8MI_ERR_UNSUPPORTED;
+  fp8mi::GemmParams p{reinterpret_cast<const uint8_t*>(a), 0, nullptr, lda, reinterpret_cast<const uint8_t*>(b), 0,
+                      nullptr, ldb, FP8MI_GEMM_TENSOR, M, N, K, c, c_dtype, ldc};
+  return hip_status(fp8mi::launch_gemm_bf16(p, (hipStream_t)stream));
+}
+
 const char* fp8_status_string(int status) {
   switch (status) {
     case FP8MI_OK: return "ok";
@@ -127,6 +147,6 @@ const char* fp8_status_string(int status) {
   return "unknown status";
 }
 
-int fp8_version(void) { return 200; }
+int fp8_version(void) { return 300; }
 
 }  // extern "C"

@@ -26,6 +26,12 @@
 // keeps STAGES - 1 steps of loads in flight behind the MFMAs, with one
 // workgroup barrier per step.
 //
+// The same kernel, with BF16 operands and v_mfma_f32_16x16x32_bf16, is the
+// BF16 GEMM FP8's speedup is measured against ("Mastering FP8 LLM training",
+// Fig. 1): a 128-byte K step is 64 BF16 elements, the two 16-byte halves of a
+// fragment feed two 32-deep products, and tiles, data movement and epilogue
+// are shared, so the two differ only in the matrix-core instruction.
+//
 // Scale application:
 //   TENSOR      one alpha = s_a * s_b on the FP32 accumulator at the end;
 //   MX          E8M0 scales fed to the scaled MFMA (no VALU work);
@@ -42,6 +48,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 128;
@@ -51,6 +58,17 @@ template <int FA, int FB>
 __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz / blgp select the operand formats: 0 = E4M3, 1 = E5M2
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+}
+
+// BF16 operands: the 32-byte fragment holds K elements [8g, 8g+8) and
+// [32+8g, 32+8g+8) of lane group g; A and B use the same lane -> K map, so
+// two 32-deep products cover the 64-deep step.
+__device__ __forceinline__ v4f mfma_bf16(const v8i& a, const v8i& b, v4f c) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i a0 = {a[0], a[1], a[2], a[3]}, a1 = {a[4], a[5], a[6], a[7]};
+  const v4i b0 = {b[0], b[1], b[2], b[3]}, b1 = {b[4], b[5], b[6], b[7]};
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v8bf, b0), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v8bf, b1), c, 0, 0, 0);
 }
 
 // MX tile step: acc[i][j] += B-fragment j x A-fragment i (the C^T form) with
@@ -126,10 +144,10 @@ template <int REC>
 struct ScaleTraits {
   // dwords staged per K step for A and for B (float bits or 4 packed E8M0 bytes)
   template <int BM>
-  static constexpr int a_words() { return REC == kGemmTensor ? 0 : BM; }
+  static constexpr int a_words() { return (REC == kGemmTensor || REC == kGemmBf16) ? 0 : BM; }
   template <int BN>
   static constexpr int b_words() {
-    return REC == kGemmTensor ? 0 : (REC == kGemmBlock128x128 ? (BN + 127) / 128 : BN);
+    return (REC == kGemmTensor || REC == kGemmBf16) ? 0 : (REC == kGemmBlock128x128 ? (BN + 127) / 128 : BN);
   }
 };
 
@@ -390,7 +408,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   // The MFMA computes C^T tiles (B fragment first): lane (lr, lg) then holds
   // row i*16 + lr and columns lg*CPL + 4j + r of the wave tile.
   auto compute = [&]() {
-    if constexpr (REC == kGemmTensor) {
+    if constexpr (REC == kGemmTensor || REC == kGemmBf16) {
       // A fragment i + 1 is read while sub-tile row i computes; one
       // scheduling region per row keeps two A fragments live
       load_fa(0);
@@ -398,7 +416,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       for (int i = 0; i < MT; ++i) {
         if (i + 1 < MT) load_fa(i + 1);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = (REC == kGemmBf16) ? mfma_bf16(fb[j], fa[i], acc[i][j]) : mfma<FB, FA>(fb[j], fa[i], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (kBlock) {
@@ -597,6 +616,17 @@ hipError_t launch_fmt(const GemmParams& g, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_bf16(const GemmParams& g, hipStream_t st) {
+  // BF16 operands through the byte-addressed kernel: K and the leading
+  // dimensions in bytes, no scales
+  GemmParams b = g;
+  b.K = 2 * g.K;
+  b.lda = 2 * g.lda;
+  b.ldb = 2 * g.ldb;
+  return g.c_dtype == kOutBf16 ? launch4<kE4M3, kE4M3, kGemmBf16, kOutBf16>(b, st)
+                               : launch4<kE4M3, kE4M3, kGemmBf16, kOutFp32>(b, st);
+}
 
 hipError_t launch_gemm(const GemmParams& g, hipStream_t st) {
   if (g.fmt_a == kE4M3)

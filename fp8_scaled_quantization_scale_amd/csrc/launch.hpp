@@ -13,6 +13,8 @@ constexpr int kOutBf16 = 0, kOutFp32 = 1;
 constexpr int kRecipeTensorCurrent = 0, kRecipeTensorDelayed = 1, kRecipeBlock1x128 = 2,
               kRecipeBlock128x128 = 3, kRecipeMx1x32 = 4;
 constexpr int kGemmTensor = 0, kGemmBlock128x128 = 1, kGemmBlock1x128 = 2, kGemmMx = 3;
+// internal: BF16 operands, no scales (fp8_bf16_gemm)
+constexpr int kGemmBf16 = 4;
 // slots of a delayed-scaling amax accumulator (FP8MI_AMAX_SLOTS)
 constexpr int kAmaxSlots = 1024;
 
@@ -54,5 +56,7 @@ hipError_t launch_empty_scale(float* amax, float* scale, float* scale_inv, hipSt
 hipError_t launch_history(float* history, int32_t* head, int len, float* amax, int fmt, int margin,
                           float* scale, float* scale_inv, int32_t* nonfinite, hipStream_t st);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
+// a, b BF16 [M x K], [N x K]; K, lda, ldb in elements
+hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t st);
 
 }  // namespace fp8mi

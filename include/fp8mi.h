@@ -196,6 +196,22 @@ int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,
                     int recipe, int64_t M, int64_t N, int64_t K,
                     void* c, int c_dtype, int64_t ldc, void* stream);
 
+/* fp8_bf16_gemm -- C = A . B^T with BF16 operands and FP32 accumulation:
+ * the BF16 GEMM that FP8's speedup is measured against [P3 Fig. 1: FP8
+ * GEMM throughput of each scaling strategy relative to BF16, over K].  It
+ * is the fp8_gemm_scaled kernel with the BF16 matrix-core instruction in
+ * place of the FP8 one: same tiles, data movement and epilogue.
+ *
+ *   a [M x K] BF16, lda; b [N x K] BF16, ldb (elements, K contiguous);
+ *   c [M x N] (c_dtype), ldc.  C[i][j] = sum_k a[i][k] * b[j][k].
+ * Requirements: M, N, K >= 0; K % 8 == 0; a, b 16-byte aligned, lda, ldb
+ * multiples of 8, K <= lda, ldb <= 2097152 (else FP8MI_ERR_UNSUPPORTED);
+ * ldc >= N.  K == 0 writes zeros.  Errors as for fp8_gemm_scaled.
+ * Tolerance vs a float64 reference: as fp8_gemm_scaled. */
+int fp8_bf16_gemm(const void* a, int64_t lda, const void* b, int64_t ldb,
+                  int64_t M, int64_t N, int64_t K,
+                  void* c, int c_dtype, int64_t ldc, void* stream);
+
 /* Human-readable text of a status code; for FP8MI_ERR_HIP the text of the
  * last HIP error seen by this thread.  The string is owned by the library. */
 const char* fp8_status_string(int status);

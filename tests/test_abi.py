@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (fp8_\w+)$", out, flags=re.M))
     assert set(_declared()) <= exported
-    assert fm.version() == 200
+    assert fm.version() == 300
     assert fm.status_string(fm.ERR_ALIGN).startswith("pointer")
 
 
@@ -126,3 +126,31 @@ def test_history_validation():
     assert f(None, GOOD, 200, GOOD, 0, 0, GOOD, GOOD, None, 0) == fm.ERR_NULL
     assert f(GOOD, GOOD, 0, GOOD, 0, 0, GOOD, GOOD, None, 0) == fm.ERR_SHAPE
     assert f(GOOD, GOOD, 200, GOOD, 0, -1, GOOD, GOOD, None, 0) == fm.ERR_SHAPE
+
+
+def _b(**kw):
+    args = dict(a=GOOD, lda=256, b=GOOD, ldb=256, M=128, N=128, K=256, c=GOOD, c_dtype=fm.OUT_BF16,
+                ldc=128, stream=0)
+    args.update(kw)
+    return fm.fp8_bf16_gemm(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c_dtype=2), fm.ERR_ENUM),
+    (dict(K=-8), fm.ERR_SHAPE),
+    (dict(c=None), fm.ERR_NULL),
+    (dict(b=None), fm.ERR_NULL),
+    (dict(K=252), fm.ERR_SHAPE),
+    (dict(ldb=128), fm.ERR_SHAPE),
+    (dict(ldc=64), fm.ERR_SHAPE),
+    (dict(a=GOOD + 8), fm.ERR_ALIGN),
+    (dict(lda=260), fm.ERR_ALIGN),
+    (dict(lda=(1 << 21) + 8), fm.ERR_UNSUPPORTED),
+])
+def test_bf16_gemm_validation(kw, code):
+    assert _b(**kw) == code
+
+
+def test_bf16_gemm_empty_is_ok_without_launch():
+    assert _b(M=0) == fm.OK
+    assert _b(N=0, c=None) == fm.OK

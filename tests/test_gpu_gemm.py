@@ -136,3 +136,38 @@ def test_ldc_and_strided_output():
     fm.gemm(a, fm.E4M3, sa, b, fm.E4M3, sb, fm.GEMM_BLOCK_1x128_1x128, K, M=M, N=N, c=big)
     _check(big[:, :N], da, db, "fp32")
     assert torch.all(big[:, N:] == -1.0)
+
+
+# ---------------------------------------------------------------------------
+# the BF16 GEMM the FP8 speedup is measured against
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out", [fm.OUT_BF16, fm.OUT_FP32])
+def test_bf16_gemm_matches_reference(out):
+    """BF16 operands are exact in float64, so C_ref is their float64 product."""
+    need_gpu()
+    name, dt = OUT[out]
+    for i, (M, N, K) in enumerate(SHAPES + [(300, 520, 2056)]):
+        a = workloads.make(workloads.Tensor("A", M, K, "outliers", 1.0, 2000 + i, 0.02, 50.0))
+        b = workloads.make(workloads.Tensor("B", N, K, "normal", 0.02, 2100 + i))
+        c = fm.bf16_gemm(a.cuda(), b.cuda(), dt)
+        _check(c, a.double().numpy(), b.double().numpy(), name)
+
+
+def test_bf16_gemm_exact_small_integers_and_padding():
+    """Small-integer operands (exact FP32 sums) compared bit for bit, with
+    padded leading dimensions whose padding holds large values."""
+    need_gpu()
+    rng = np.random.default_rng(9)
+    M, N, K = 272, 144, 392
+    va = rng.integers(-8, 9, (M, K + 24)).astype(np.float32)
+    vb = rng.integers(-8, 9, (N, K + 8)).astype(np.float32)
+    va[:, K:] = 3e4
+    vb[:, K:] = -3e4
+    a = torch.from_numpy(va).to(torch.bfloat16).cuda()
+    b = torch.from_numpy(vb).to(torch.bfloat16).cuda()
+    c = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    st = fm.fp8_bf16_gemm(a, K + 24, b, K + 8, M, N, K, c, fm.OUT_FP32, N)
+    assert st == fm.OK
+    want = va[:, :K].astype(np.float64) @ vb[:, :K].astype(np.float64).T
+    assert np.array_equal(host(c).astype(np.float64), want)

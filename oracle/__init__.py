@@ -77,6 +77,10 @@ def _load():
     lib.or_e8m0_value.argtypes = [i32]
     lib.or_quantize_mx.restype = i64
     lib.or_quantize_mx.argtypes = [i32, vp, i64, i64, i64, i64, vp, vp]
+    lib.or_mx_scale_byte_floor.restype = i32
+    lib.or_mx_scale_byte_floor.argtypes = [i32, f32]
+    lib.or_quantize_mx_rule.restype = i64
+    lib.or_quantize_mx_rule.argtypes = [i32, vp, i64, i64, i64, i64, i32, vp, vp]
     lib.or_history_update.restype = i32
     lib.or_history_update.argtypes = [vp, vp, i32, f32, i32, i32, vp, vp, vp]
     _lib = lib
@@ -180,22 +184,36 @@ def quantize_blocks(fmt: str, x, br: int, bc: int, margin: int = 0):
     return q, grid, bad
 
 
-def mx_scale_byte(fmt: str, amax_value: float) -> int:
-    return _load().or_mx_scale_byte(_FMT[fmt], float(np.float32(amax_value)))
+def mx_scale_byte(fmt: str, amax_value: float, rule: str = "ceil") -> int:
+    """E8M0 byte of a block amax: "ceil" = smallest power of two with no
+    element saturating; "floor" = the OCP specification's floor(log2 amax) - emax."""
+    f = _load().or_mx_scale_byte_floor if rule == "floor" else _load().or_mx_scale_byte
+    return f(_FMT[fmt], float(np.float32(amax_value)))
 
 
 def e8m0_value(byte: int) -> float:
     return _load().or_e8m0_value(int(byte))
 
 
-def quantize_mx(fmt: str, x, br: int, bc: int):
+def quantize_mx(fmt: str, x, br: int, bc: int, rule: str = "ceil"):
     """MX blocks of br x bc with E8M0 scale bytes -> (codes, bytes, n_nonfinite)."""
+    assert rule in ("ceil", "floor")
     a = _f32(x)
     r, c = a.shape
     q = np.empty(a.shape, np.uint8)
     grid = np.empty(((r + br - 1) // br, (c + bc - 1) // bc), np.uint8)
-    bad = _load().or_quantize_mx(_FMT[fmt], _ptr(a), r, c, br, bc, _ptr(q), _ptr(grid))
+    bad = _load().or_quantize_mx_rule(_FMT[fmt], _ptr(a), r, c, br, bc, int(rule == "floor"),
+                                      _ptr(q), _ptr(grid))
     return q, grid, bad
+
+
+def quantize_channel(fmt: str, x, margin: int = 0):
+    """Channel-wise scaling: one scale per row, i.e. block scaling with
+    1 x cols blocks -> (codes, s_inv [rows], n_nonfinite).  Per-column
+    scales are quantize_channel of the transpose."""
+    a = _f32(x)
+    q, grid, bad = quantize_blocks(fmt, a, 1, max(a.shape[1], 1), margin)
+    return q, grid[:, 0].copy(), bad
 
 
 class History:

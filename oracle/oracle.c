@@ -36,7 +36,12 @@
  *     amax == 0 -> s = 1; non-finite amax -> s = 1 and a flag; s = +Inf
  *     (tiny amax) -> FLT_MAX.
  *   - MX: E8M0 exponent e = ceil(log2(amax / max)), clamped to [-127, 127],
- *     stored as e + 127; amax == 0 -> 127; non-finite amax -> 0xFF.
+ *     stored as e + 127; amax == 0 -> 127; non-finite amax -> 0xFF.  The
+ *     OCP specification's floor rule (e = floor(log2 amax) - emax) is a
+ *     variant, selected per call.
+ *   - Channel-wise scaling ("Mastering FP8 LLM training", Fig. 1 discussion:
+ *     one scale per channel, i.e. per row or column) is block scaling with
+ *     1 x cols blocks; it needs no code of its own here.
  */
 #include <float.h>
 #include <math.h>
@@ -284,6 +289,27 @@ int or_mx_scale_byte(int fmt, float amax)
     return e + 127;
 }
 
+/* The OCP microscaling specification's rule, kept beside the one above as
+ * a variant: the shared exponent is floor(log2(amax)) - emax, i.e. e = E -
+ * emax for every f, so a block whose largest element has f > 1.75 saturates
+ * that element to max instead of taking the next power of two.  Zero and
+ * non-finite amax as above. */
+int or_mx_scale_byte_floor(int fmt, float amax)
+{
+    if (!isfinite(amax))
+        return 0xFF;
+    if (amax == 0.0f)
+        return 127;
+    int E2;
+    frexp((double)amax, &E2); /* amax = f * 2^E2, f in [0.5, 1) */
+    int e = (E2 - 1) - (fmt == OR_E4M3 ? 8 : 15);
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e + 127;
+}
+
 /* 2^(byte - 127) as the dequantisation scale of an E8M0 byte; NaN for 0xFF. */
 double or_e8m0_value(int byte)
 {
@@ -295,8 +321,8 @@ double or_e8m0_value(int byte)
 /* MX quantize: blocks of br x bc (1x32 along a row or 32x1 down a column).
  * Elements are enc(fl32(x * 2^-e)); a non-finite block amax gives scale
  * byte 0xFF and elements enc(x). */
-int64_t or_quantize_mx(int fmt, const float* x, int64_t rows, int64_t cols, int64_t br, int64_t bc,
-                       uint8_t* q, uint8_t* scale_bytes)
+int64_t or_quantize_mx_rule(int fmt, const float* x, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                            int floor_rule, uint8_t* q, uint8_t* scale_bytes)
 {
     int64_t gr = (rows + br - 1) / br, gc = (cols + bc - 1) / bc, bad = 0;
     for (int64_t bi = 0; bi < gr; ++bi)
@@ -304,7 +330,7 @@ int64_t or_quantize_mx(int fmt, const float* x, int64_t rows, int64_t cols, int6
             int64_t r0 = bi * br, r1 = r0 + br < rows ? r0 + br : rows;
             int64_t c0 = bj * bc, c1 = c0 + bc < cols ? c0 + bc : cols;
             float amax = or_amax_block(x, cols, r0, r1, c0, c1);
-            int byte = or_mx_scale_byte(fmt, amax);
+            int byte = floor_rule ? or_mx_scale_byte_floor(fmt, amax) : or_mx_scale_byte(fmt, amax);
             float s = 1.0f;
             if (byte == 0xFF)
                 bad += 1;
@@ -314,6 +340,12 @@ int64_t or_quantize_mx(int fmt, const float* x, int64_t rows, int64_t cols, int6
             scale_bytes[bi * gc + bj] = (uint8_t)byte;
         }
     return bad;
+}
+
+int64_t or_quantize_mx(int fmt, const float* x, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                       uint8_t* q, uint8_t* scale_bytes)
+{
+    return or_quantize_mx_rule(fmt, x, rows, cols, br, bc, 0, q, scale_bytes);
 }
 
 /* ------------------------------------------------------------------ */

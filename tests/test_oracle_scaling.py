@@ -211,6 +211,53 @@ def test_mx_quantize_matches_torch(br, bc):
     assert sb[0, 0] == 127 if br == 1 else True
 
 
+@pytest.mark.parametrize("fmt", oracle.FORMATS)
+def test_mx_floor_rule_closed_form(fmt):
+    """OCP floor rule: e = floor(log2 amax) - emax (emax 8 for E4M3, 15 for
+    E5M2), computed here from Python's exact frexp, clamped to [-127, 127]."""
+    emax = 8 if fmt == "e4m3" else 15
+    bits = (np.arange(1, 0x7F80, 3, dtype=np.uint32) << 16)
+    for a in bits.view(np.float32):
+        _, E = np.frexp(np.float64(a))  # a = f 2^E, f in [0.5, 1)
+        e = min(max(int(E) - 1 - emax, -127), 127)
+        assert oracle.mx_scale_byte(fmt, a, "floor") == e + 127, a
+        # the two rules differ exactly when the significand exceeds max's
+        ceil_b = oracle.mx_scale_byte(fmt, a)
+        f = np.float64(a) / 2.0 ** (int(E) - 1)
+        if -127 < e < 126:
+            assert ceil_b - (e + 127) == (1 if f > 1.75 else 0), a
+    assert oracle.mx_scale_byte(fmt, 0.0, "floor") == 127
+    assert oracle.mx_scale_byte(fmt, np.nan, "floor") == 255
+
+
+def test_mx_floor_rule_saturates_the_top_binade():
+    """A block whose amax lies in (448, 512) keeps e = 0 under the floor rule:
+    those elements saturate to 448 (code 0x7E), the ceil rule halves them."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [480.0, -500.0, 448.0, 1.0]
+    qf, bf, _ = oracle.quantize_mx("e4m3", x, 1, 32, "floor")
+    qc, bc, _ = oracle.quantize_mx("e4m3", x, 1, 32)
+    assert bf[0, 0] == 127 and bc[0, 0] == 128
+    assert list(qf[0, :4]) == [0x7E, 0xFE, 0x7E, oracle.encode("e4m3", np.float32([1.0]))[0]]
+    assert list(oracle.decode("e4m3", qc[0, :4])) == [240.0, -256.0, 224.0, 0.5]
+
+
+def test_channel_scaling_is_current_scaling_per_row():
+    """One scale per row: each row equals per-tensor current scaling of that
+    row alone; per-column scales are the rows of the transpose."""
+    x = workloads.make(workloads.Tensor("X", 64, 520, "gains", 1.0, 15))
+    x[5, :] = 0
+    q, si, bad = oracle.quantize_channel("e4m3", x)
+    assert bad == 0 and si.shape == (64,) and si[5] == 1.0
+    for r in (0, 5, 17, 63):
+        qr, _, sir, _, _ = oracle.quantize_current("e4m3", x[r:r + 1])
+        assert np.array_equal(q[r:r + 1], qr) and si[r] == sir
+    qt, sit, _ = oracle.quantize_channel("e5m2", x.t().contiguous())
+    for c in (0, 300, 519):
+        qc, _, sic, _, _ = oracle.quantize_current("e5m2", x[:, c:c + 1])
+        assert np.array_equal(qt[c], qc[:, 0]) and sit[c] == sic
+
+
 # ---------------------------------------------------------------------------
 # amax history [2025 technical guide sec. 2.1; From FP16 to FP8 sec. 3.3]
 # ---------------------------------------------------------------------------

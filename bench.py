@@ -437,6 +437,8 @@ def speedup_sweep(M: int, N: int, ks, reps: int):
     hipBLASLt's BF16 GEMM (torch.matmul) is timed beside it for context."""
     ev = HipEvents(1)
     recipes = (("tensor", fm.TENSOR_CURRENT, fm.TENSOR_CURRENT, fm.GEMM_TENSOR),
+               ("channel", fm.CHANNEL, fm.CHANNEL, fm.GEMM_CHANNEL),
+               ("128x128_128x128", fm.BLOCK_128x128, fm.BLOCK_128x128, fm.GEMM_BLOCK_128x128_128x128),
                ("1x128_128x128", fm.BLOCK_1x128, fm.BLOCK_128x128, fm.GEMM_BLOCK_1x128_128x128),
                ("1x128_1x128", fm.BLOCK_1x128, fm.BLOCK_1x128, fm.GEMM_BLOCK_1x128_1x128),
                ("mx_1x32", fm.MX_1x32, fm.MX_1x32, fm.GEMM_MX_1x32))

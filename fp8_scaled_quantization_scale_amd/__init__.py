@@ -29,8 +29,10 @@ E4M3, E5M2 = 0, 1
 IN_BF16, IN_FP32 = 0, 1
 OUT_BF16, OUT_FP32 = 0, 1
 TENSOR_CURRENT, TENSOR_DELAYED, BLOCK_1x128, BLOCK_128x128, MX_1x32 = 0, 1, 2, 3, 4
+CHANNEL, MX_1x32_OCP = 5, 6
 ROW, COL, ROW_AND_COL = 1, 2, 3
 GEMM_TENSOR, GEMM_BLOCK_1x128_128x128, GEMM_BLOCK_1x128_1x128, GEMM_MX_1x32 = 0, 1, 2, 3
+GEMM_BLOCK_128x128_128x128, GEMM_CHANNEL = 4, 5
 AMAX_SLOTS = 1024  # floats in a delayed-scaling amax accumulator
 
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
@@ -166,8 +168,10 @@ def scale_grid_shape(recipe: int, rows: int, cols: int, orient: int):
     if recipe == BLOCK_128x128:
         g = (_ceil(rows, 128), _ceil(cols, 128))
         return (g if orient == ROW else (g[1], g[0])), torch.float32
-    if recipe == MX_1x32:
+    if recipe in (MX_1x32, MX_1x32_OCP):
         return ((rows, _ceil(cols, 32)) if orient == ROW else (cols, _ceil(rows, 32))), torch.uint8
+    if recipe == CHANNEL:
+        return ((rows,) if orient == ROW else (cols,)), torch.float32
     return None, None
 
 

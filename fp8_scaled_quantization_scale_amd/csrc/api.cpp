@@ -26,7 +26,7 @@ int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
                    const void* s_row, const uint8_t* q_col, int64_t ld_q_col, const void* s_col,
                    const float* scale, const float* scale_inv, const float* amax) {
   if (x_dtype != FP8MI_IN_BF16 && x_dtype != FP8MI_IN_FP32) return FP8MI_ERR_ENUM;
-  if (recipe < FP8MI_TENSOR_CURRENT || recipe > FP8MI_MX_1x32) return FP8MI_ERR_ENUM;
+  if (recipe < FP8MI_TENSOR_CURRENT || recipe > FP8MI_MX_1x32_OCP) return FP8MI_ERR_ENUM;
   if (fmt != FP8MI_E4M3 && fmt != FP8MI_E5M2) return FP8MI_ERR_ENUM;
   if (orient != FP8MI_ROW && orient != FP8MI_COL && orient != FP8MI_ROW_AND_COL) return FP8MI_ERR_ENUM;
   if (rows < 0 || cols < 0 || margin < 0 || margin > 64) return FP8MI_ERR_SHAPE;
@@ -51,6 +51,9 @@ int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
   if (col && (!aligned16(q_col) || ld_q_col % 16)) return FP8MI_ERR_ALIGN;
   // grid limits of the tile launch (128 x 128 tiles, 2-D grid)
   if ((rows + 127) / 128 > 65535 || (cols + 127) / 128 > 0x7FFFFFFF) return FP8MI_ERR_UNSUPPORTED;
+  // channel scaling launches one workgroup per tile on a 1-D grid
+  if (recipe == FP8MI_CHANNEL && ((rows + 127) / 128) * ((cols + 127) / 128) > 0x7FFFFFFF)
+    return FP8MI_ERR_UNSUPPORTED;
   return FP8MI_OK;
 }
 
@@ -59,7 +62,7 @@ int check_gemm(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const 
                int c_dtype, int64_t ldc) {
   if (fmt_a != FP8MI_E4M3 && fmt_a != FP8MI_E5M2) return FP8MI_ERR_ENUM;
   if (fmt_b != FP8MI_E4M3 && fmt_b != FP8MI_E5M2) return FP8MI_ERR_ENUM;
-  if (recipe < FP8MI_GEMM_TENSOR || recipe > FP8MI_GEMM_MX_1x32) return FP8MI_ERR_ENUM;
+  if (recipe < FP8MI_GEMM_TENSOR || recipe > FP8MI_GEMM_CHANNEL) return FP8MI_ERR_ENUM;
   if (c_dtype != FP8MI_OUT_BF16 && c_dtype != FP8MI_OUT_FP32) return FP8MI_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0) return FP8MI_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8MI_OK;

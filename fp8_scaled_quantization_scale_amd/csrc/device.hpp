@@ -60,6 +60,18 @@ __device__ __forceinline__ int mx_scale_byte(float amax) {
   return e + 127;
 }
 
+// The OCP microscaling specification's exponent rule: floor(log2(amax)) -
+// emax, whatever the significand, so a block whose largest element lies
+// above max * 2^e saturates it (zero and non-finite amax as above).
+template <int FMT>
+__device__ __forceinline__ int mx_scale_byte_floor(float amax) {
+  if (!is_finite(amax)) return 0xFF;
+  if (amax == 0.0f) return 127;
+  int e = __builtin_amdgcn_frexp_expf(amax) - 1 - Fmt<FMT>::kEmax;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return e + 127;
+}
+
 // 2^-(byte-127) as a binary32 (byte in [0, 254]); 2^127 .. 2^-127 are all
 // representable (2^-127 as a subnormal).
 __device__ __forceinline__ float mx_inv_scale(int byte) {

@@ -34,6 +34,7 @@
 //
 // Scale application:
 //   TENSOR      one alpha = s_a * s_b on the FP32 accumulator at the end;
+//   CHANNEL     s_a[row] * s_b[col] on the FP32 accumulator at the end;
 //   MX          E8M0 scales fed to the scaled MFMA (no VALU work);
 //   BLOCK_*     each 128-deep K block is an MFMA into a zeroed FP32 partial,
 //               then acc += (s_a[row, kb] * s_b[.., kb]) * partial on the VALU.
@@ -142,12 +143,15 @@ struct GArgs {
 
 template <int REC>
 struct ScaleTraits {
-  // dwords staged per K step for A and for B (float bits or 4 packed E8M0 bytes)
+  // dwords staged per K step for A and for B (float bits or 4 packed E8M0
+  // bytes).  2-D A tiles need BM / 128 words, padded to a whole wave so that
+  // B's words start on a wave boundary (the padding reads past the grid: zero).
+  static constexpr bool kNone = REC == kGemmTensor || REC == kGemmBf16 || REC == kGemmChannel;
   template <int BM>
-  static constexpr int a_words() { return (REC == kGemmTensor || REC == kGemmBf16) ? 0 : BM; }
+  static constexpr int a_words() { return kNone ? 0 : (REC == kGemmBlock2d ? 64 : BM); }
   template <int BN>
   static constexpr int b_words() {
-    return (REC == kGemmTensor || REC == kGemmBf16) ? 0 : (REC == kGemmBlock128x128 ? (BN + 127) / 128 : BN);
+    return kNone ? 0 : ((REC == kGemmBlock128x128 || REC == kGemmBlock2d) ? (BN + 127) / 128 : BN);
   }
 };
 
@@ -179,7 +183,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   constexpr int SA_W = ScaleTraits<REC>::template a_words<BM>();
   constexpr int SB_W = ScaleTraits<REC>::template b_words<BN>();
   constexpr int S_W = SA_W + SB_W;
-  constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128;
+  constexpr bool kBlock = REC == kGemmBlock128x128 || REC == kGemmBlock1x128 || REC == kGemmBlock2d;
+  constexpr bool kTileB = REC == kGemmBlock128x128 || REC == kGemmBlock2d;  // B scales per 128x128 tile
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * TILE_BYTES];
   constexpr bool kMx = REC == kGemmMx;
@@ -253,8 +258,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   int nkb = 0;
   if constexpr (kBlock) {
     nkb = KT;
-    rsa = make_rsrc(reinterpret_cast<const uint32_t*>(p.sa) + (int64_t)m0 * nkb, (uint32_t)(rows_a * nkb * 4));
-    if constexpr (REC == kGemmBlock128x128) {
+    if constexpr (REC == kGemmBlock2d)
+      rsa = make_rsrc(reinterpret_cast<const uint32_t*>(p.sa) + (int64_t)(m0 / 128) * nkb,
+                      (uint32_t)(((rows_a + 127) / 128) * nkb * 4));
+    else
+      rsa = make_rsrc(reinterpret_cast<const uint32_t*>(p.sa) + (int64_t)m0 * nkb, (uint32_t)(rows_a * nkb * 4));
+    if constexpr (kTileB) {
       const int tb = (rows_b + 127) / 128;
       rsb = make_rsrc(reinterpret_cast<const uint32_t*>(p.sb) + (int64_t)(n0 / 128) * nkb, (uint32_t)(tb * nkb * 4));
     } else {
@@ -385,9 +394,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       fb[j] = frag(lb, row, swz_b(row));
     }
     if constexpr (kBlock) {
+      if constexpr (REC == kGemmBlock2d) {
+        static_assert(WM <= 128 && 128 % WM == 0, "a wave's rows lie inside one 128-row A tile");
+        const float sav = __builtin_bit_cast(float, sscale[st][(wm * WM) / 128]);
 #pragma unroll
-      for (int i = 0; i < MT; ++i) bsa[i] = __builtin_bit_cast(float, sscale[st][wm * WM + i * 16 + lr]);
-      if constexpr (REC == kGemmBlock128x128) {
+        for (int i = 0; i < MT; ++i) bsa[i] = sav;
+      } else {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) bsa[i] = __builtin_bit_cast(float, sscale[st][wm * WM + i * 16 + lr]);
+      }
+      if constexpr (kTileB) {
         static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie inside one 128-wide B tile");
         const float sbv = __builtin_bit_cast(float, sscale[st][SA_W + (wn * WN) / 128]);
 #pragma unroll
@@ -408,7 +424,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   // The MFMA computes C^T tiles (B fragment first): lane (lr, lg) then holds
   // row i*16 + lr and columns lg*CPL + 4j + r of the wave tile.
   auto compute = [&]() {
-    if constexpr (REC == kGemmTensor || REC == kGemmBf16) {
+    if constexpr (REC == kGemmTensor || REC == kGemmBf16 || REC == kGemmChannel) {
       // A fragment i + 1 is read while sub-tile row i computes; one
       // scheduling region per row keeps two A fragments live
       load_fa(0);
@@ -438,7 +454,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
           const int q = k - LAG, i = q / NT, j = q % NT;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float sc = (REC == kGemmBlock128x128) ? bsa[i] : bsa[i] * bsb[j][r];
+            const float sc = kTileB ? bsa[i] : bsa[i] * bsb[j][r];
             acc[i][j][r] = __builtin_fmaf(part[q % (LAG + 1)][r], sc, acc[i][j][r]);
           }
         }
@@ -509,15 +525,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   constexpr int ESIZE = OUT == kOutBf16 ? 2 : 4;
   const bool vec_ok = ((p.ldc * ESIZE) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
   const int cbase = n0 + wn * WN + lg * CPL;
+  // channel scaling: s_b of this lane's CPL columns, s_a per row below
+  float csb[REC == kGemmChannel ? CPL : 1];
+  if constexpr (REC == kGemmChannel) {
+    const float* sb = reinterpret_cast<const float*>(p.sb);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) csb[c] = (KT > 0 && cbase + c < p.N) ? sb[cbase + c] : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int row = m0 + wm * WM + i * 16 + lr;
     if (row >= p.M) continue;
     float v[CPL];
+    if constexpr (REC == kGemmChannel) {
+      const float sar = KT > 0 ? reinterpret_cast<const float*>(p.sa)[row] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * j + r] = (REC == kGemmTensor) ? acc[i][j][r] * alpha : acc[i][j][r];
+        for (int r = 0; r < 4; ++r) v[4 * j + r] = acc[i][j][r] * (sar * csb[4 * j + r]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[4 * j + r] = (REC == kGemmTensor) ? acc[i][j][r] * alpha : acc[i][j][r];
+    }
     if constexpr (OUT == kOutBf16) {
       __bf16* dst = reinterpret_cast<__bf16*>(p.c) + (int64_t)row * p.ldc + cbase;
       if (vec_ok && cbase + CPL <= p.N) {
@@ -611,6 +642,10 @@ hipError_t launch_fmt(const GemmParams& g, hipStream_t st) {
                 : launch4<FA, FB, kGemmBlock1x128, kOutFp32>(g, st);
     case kGemmMx:
       return bf ? launch4<FA, FB, kGemmMx, kOutBf16>(g, st) : launch4<FA, FB, kGemmMx, kOutFp32>(g, st);
+    case kGemmBlock2d:
+      return bf ? launch4<FA, FB, kGemmBlock2d, kOutBf16>(g, st) : launch4<FA, FB, kGemmBlock2d, kOutFp32>(g, st);
+    case kGemmChannel:
+      return bf ? launch4<FA, FB, kGemmChannel, kOutBf16>(g, st) : launch4<FA, FB, kGemmChannel, kOutFp32>(g, st);
   }
   return hipErrorInvalidValue;
 }

@@ -11,10 +11,11 @@ namespace fp8mi {
 constexpr int kInBf16 = 0, kInFp32 = 1;
 constexpr int kOutBf16 = 0, kOutFp32 = 1;
 constexpr int kRecipeTensorCurrent = 0, kRecipeTensorDelayed = 1, kRecipeBlock1x128 = 2,
-              kRecipeBlock128x128 = 3, kRecipeMx1x32 = 4;
-constexpr int kGemmTensor = 0, kGemmBlock128x128 = 1, kGemmBlock1x128 = 2, kGemmMx = 3;
+              kRecipeBlock128x128 = 3, kRecipeMx1x32 = 4, kRecipeChannel = 5, kRecipeMx1x32Ocp = 6;
+constexpr int kGemmTensor = 0, kGemmBlock128x128 = 1, kGemmBlock1x128 = 2, kGemmMx = 3, kGemmBlock2d = 4,
+              kGemmChannel = 5;
 // internal: BF16 operands, no scales (fp8_bf16_gemm)
-constexpr int kGemmBf16 = 4;
+constexpr int kGemmBf16 = 16;
 // slots of a delayed-scaling amax accumulator (FP8MI_AMAX_SLOTS)
 constexpr int kAmaxSlots = 1024;
 

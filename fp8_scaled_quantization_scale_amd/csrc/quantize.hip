@@ -63,7 +63,19 @@ __device__ __forceinline__ void st_stream8(void* p, uint2 w) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
-enum : int { MODE_TENSOR = 0, MODE_B1x128 = 1, MODE_B128x128 = 2, MODE_MX32 = 3 };
+enum : int { MODE_TENSOR = 0, MODE_B1x128 = 1, MODE_B128x128 = 2, MODE_MX32 = 3, MODE_CHANNEL = 4, MODE_MX32F = 5 };
+
+// E8M0 byte of an MX block: MODE_MX32 takes the smallest power of two under
+// which no element saturates, MODE_MX32F the OCP specification's floor rule.
+template <int MODE, int FMT>
+__device__ __forceinline__ int mx_byte(float amax) {
+  if constexpr (MODE == MODE_MX32F) return mx_scale_byte_floor<FMT>(amax);
+  else return mx_scale_byte<FMT>(amax);
+}
+// Channel scales travel between the passes as the scale s itself, with the
+// sign bit marking a row / column whose amax was not finite (s = 1 there).
+__device__ __forceinline__ float chan_s(float v) { return __builtin_fabsf(v); }
+__device__ __forceinline__ bool chan_bad(float v) { return __builtin_signbit(v) != 0; }
 
 template <typename InT>
 struct In;
@@ -340,20 +352,25 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
             reinterpret_cast<float*>(a.s_row)[r * tiles_x + bx] = recip_rn(s);
             if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
           }
-        } else if constexpr (MODE == MODE_MX32) {
+        } else if constexpr (MODE == MODE_MX32 || MODE == MODE_MX32F) {
           const uint32_t k = group_max_u32<4>(cur.key(i, v));
-          const int byte = mx_scale_byte<FMT>(key_to_float(k));
-          safe = byte == 0xFF;
-          s = safe ? 1.0f : mx_inv_scale(byte);
+          const int byte = mx_byte<MODE, FMT>(key_to_float(k));
+          // the floor rule lets elements exceed max: saturating encoder
+          safe = byte == 0xFF || MODE == MODE_MX32F;
+          s = byte == 0xFF ? 1.0f : mx_inv_scale(byte);
           if ((li & 3) == 0 && r < a.rows && nval > 0) {
             const int64_t gc = (a.cols + 31) / 32;
             reinterpret_cast<uint8_t*>(a.s_row)[r * gc + (ccol >> 5)] = (uint8_t)byte;
-            if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
+            if (byte == 0xFF && a.nonfinite) atomicAdd(a.nonfinite, 1);
           }
         } else if constexpr (MODE == MODE_TENSOR && !CURRENT) {
           const uint32_t k = cur.key(i, v);
           amax_acc = amax_acc > k ? amax_acc : k;
           safe = !fits<FMT>(k, s);
+        } else if constexpr (MODE == MODE_CHANNEL) {
+          const float sr = r < a.rows ? reinterpret_cast<const float*>(a.s_row)[r] : 1.0f;
+          s = chan_s(sr);
+          safe = chan_bad(sr);
         }
         if (r < a.rows && nval > 0) {
           uint2 c = safe ? encode8<FMT, true>(v, s) : encode8<FMT, false>(v, s);
@@ -437,23 +454,30 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
             if (safe1 && a.nonfinite) atomicAdd(a.nonfinite, 1);
           }
         }
-      } else if constexpr (MODE == MODE_MX32) {
-        const int b0 = mx_scale_byte<FMT>(key_to_float(k0));
-        const int b1 = mx_scale_byte<FMT>(key_to_float(k1));
-        safe0 = b0 == 0xFF;
-        safe1 = b1 == 0xFF;
-        s0 = safe0 ? 1.0f : mx_inv_scale(b0);
-        s1 = safe1 ? 1.0f : mx_inv_scale(b1);
+      } else if constexpr (MODE == MODE_CHANNEL) {
+        const float* sc = reinterpret_cast<const float*>(a.s_col);
+        const float v0 = colA < a.cols ? sc[colA] : 1.0f, v1 = colA + 1 < a.cols ? sc[colA + 1] : 1.0f;
+        s0 = chan_s(v0);
+        s1 = chan_s(v1);
+        safe0 = chan_bad(v0);
+        safe1 = chan_bad(v1);
+      } else if constexpr (MODE == MODE_MX32 || MODE == MODE_MX32F) {
+        const int b0 = mx_byte<MODE, FMT>(key_to_float(k0));
+        const int b1 = mx_byte<MODE, FMT>(key_to_float(k1));
+        safe0 = b0 == 0xFF || MODE == MODE_MX32F;
+        safe1 = b1 == 0xFF || MODE == MODE_MX32F;
+        s0 = b0 == 0xFF ? 1.0f : mx_inv_scale(b0);
+        s1 = b1 == 0xFF ? 1.0f : mx_inv_scale(b1);
         if (rbase < a.rows) {
           const int64_t gr = (a.rows + 31) / 32;
           uint8_t* sc = reinterpret_cast<uint8_t*>(a.s_col);
           if (colA < a.cols) {
             sc[colA * gr + (rbase >> 5)] = (uint8_t)b0;
-            if (safe0 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+            if (b0 == 0xFF && a.nonfinite) atomicAdd(a.nonfinite, 1);
           }
           if (colA + 1 < a.cols) {
             sc[(colA + 1) * gr + (rbase >> 5)] = (uint8_t)b1;
-            if (safe1 && a.nonfinite) atomicAdd(a.nonfinite, 1);
+            if (b1 == 0xFF && a.nonfinite) atomicAdd(a.nonfinite, 1);
           }
         }
       }
@@ -624,6 +648,106 @@ __global__ __launch_bounds__(kFinThreads) void amax_finalize_kernel(Slots sl, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Channel-wise scaling ("Mastering FP8 LLM training", Fig. 1 discussion: one
+// scale per channel, a row or a column): four passes.
+//   1. chan_amax_kernel: one workgroup per 128 x 128 tile stores the tile's
+//      per-row (ROW) and per-column (COL) max |x| keys as partials laid over
+//      the code outputs: row r, tile column bx at q_row[r][4 bx]; column c,
+//      tile row by at q_col[c][4 by].  When one tile spans the whole row
+//      (column) the scale is final and goes straight to s_row (s_col).
+//   2. chan_reduce_kernel: 16 lanes per row (column) fold its partials into
+//      the scale s, stored in s_row (s_col), sign bit set for a non-finite
+//      amax.
+//   3. the tile kernel casts with those scales (MODE_CHANNEL), overwriting
+//      the partials with codes.
+//   4. chan_finalize_kernel: s -> s_inv in place, counting non-finite rows.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ float chan_encode_scale(uint32_t key, int margin) {
+  const float am = key_to_float(key);
+  return is_finite(am) ? scale_from_amax<FMT>(am, margin) : -1.0f;
+}
+
+template <typename InT, int FMT, bool ROW, bool COL>
+__global__ __launch_bounds__(kThreads) void chan_amax_kernel(TileArgs a) {
+  __shared__ uint32_t colk[16][kTile];
+  const int tid = threadIdx.x;
+  const int g = tid >> 4, li = tid & 15;
+  const int64_t tiles_x = (a.cols + kTile - 1) / kTile, tiles_y = (a.rows + kTile - 1) / kTile;
+  const int64_t t = blockIdx.x;
+  const int64_t by = t / tiles_x, bx = t - by * tiles_x;
+  const int64_t row0 = by * kTile, ccol = bx * kTile + 8 * li;
+  Raw<InT> cur;
+  cur.load(reinterpret_cast<const InT*>(a.x), a.ld_x, a.rows, row0 + g, ccol, a.cols - ccol);
+  uint32_t ck[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // COL: this thread's 8 columns over its 8 rows
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[8];
+    cur.row(i, v);
+    if constexpr (ROW) {
+      const uint32_t k = group_max_u32<16>(cur.key(i, v));
+      const int64_t r = row0 + g + 16 * i;
+      if (li == 0 && r < a.rows) {
+        if (tiles_x == 1)
+          reinterpret_cast<float*>(a.s_row)[r] = chan_encode_scale<FMT>(k, a.margin);
+        else
+          *reinterpret_cast<uint32_t*>(a.q_row + r * a.ld_q_row + 4 * bx) = k;
+      }
+    }
+    if constexpr (COL) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t k = abs_key(v[e]);  // rows past the edge loaded as 0
+        ck[e] = ck[e] > k ? ck[e] : k;
+      }
+    }
+  }
+  if constexpr (COL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) colk[g][8 * li + e] = ck[e];
+    __syncthreads();
+    if (tid < kTile) {
+      uint32_t k = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) k = k > colk[q][tid] ? k : colk[q][tid];
+      const int64_t c = bx * kTile + tid;
+      if (c < a.cols) {
+        if (tiles_y == 1)
+          reinterpret_cast<float*>(a.s_col)[c] = chan_encode_scale<FMT>(k, a.margin);
+        else
+          *reinterpret_cast<uint32_t*>(a.q_col + c * a.ld_q_col + 4 * by) = k;
+      }
+    }
+  }
+}
+
+// 16 lanes per line (a row of q_row or of q_col): fold n partial keys.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void chan_reduce_kernel(const uint8_t* part, int64_t ld, int64_t lines,
+                                                               int64_t n, float* s_out, int margin) {
+  const int64_t line = (int64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  uint32_t k = 0;
+  if (line < lines) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(part + line * ld);
+    for (int64_t j = li; j < n; j += 16) k = k > p[j] ? k : p[j];
+  }
+  k = group_max_u32<16>(k);
+  if (li == 0 && line < lines) s_out[line] = chan_encode_scale<FMT>(k, margin);
+}
+
+// s -> s_inv over the row scales then the column scales
+__global__ __launch_bounds__(kThreads) void chan_finalize_kernel(float* s_row, int64_t n_row, float* s_col,
+                                                                 int64_t n_col, int32_t* nonfinite) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float* p = i < n_row ? s_row + i : (i < n_row + n_col ? s_col + (i - n_row) : nullptr);
+  if (!p) return;
+  const float v = *p;
+  *p = recip_rn(chan_s(v));
+  if (chan_bad(v) && nonfinite) atomicAdd(nonfinite, 1);
+}
+
 // Persistent grid: as many workgroups as stay resident (per the kernel's
 // register / LDS occupancy), rounded so every workgroup walks the same number
 // of tiles.
@@ -713,6 +837,34 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
       return launch_tile<InT, FMT, MODE_B128x128, false>(p, st);
     case kRecipeMx1x32:
       return launch_tile<InT, FMT, MODE_MX32, false>(p, st);
+    case kRecipeMx1x32Ocp:
+      return launch_tile<InT, FMT, MODE_MX32F, false>(p, st);
+    case kRecipeChannel: {
+      TileArgs a{p.x, p.rows, p.cols, p.ld_x, p.q_row, p.ld_q_row, p.s_row, p.q_col, p.ld_q_col,
+                 p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin};
+      const bool row = p.orient & 1, col = p.orient & 2;
+      const int64_t tx = (p.cols + kTile - 1) / kTile, ty = (p.rows + kTile - 1) / kTile;
+      const unsigned tiles = (unsigned)(tx * ty);
+      if (row && col)
+        chan_amax_kernel<InT, FMT, true, true><<<tiles, kThreads, 0, st>>>(a);
+      else if (row)
+        chan_amax_kernel<InT, FMT, true, false><<<tiles, kThreads, 0, st>>>(a);
+      else
+        chan_amax_kernel<InT, FMT, false, true><<<tiles, kThreads, 0, st>>>(a);
+      constexpr int kLines = kThreads / 16;
+      if (row && tx > 1)
+        chan_reduce_kernel<FMT><<<(unsigned)((p.rows + kLines - 1) / kLines), kThreads, 0, st>>>(
+            p.q_row, p.ld_q_row, p.rows, tx, reinterpret_cast<float*>(p.s_row), p.margin);
+      if (col && ty > 1)
+        chan_reduce_kernel<FMT><<<(unsigned)((p.cols + kLines - 1) / kLines), kThreads, 0, st>>>(
+            p.q_col, p.ld_q_col, p.cols, ty, reinterpret_cast<float*>(p.s_col), p.margin);
+      const hipError_t e = launch_tile<InT, FMT, MODE_CHANNEL, false>(p, st);
+      if (e != hipSuccess) return e;
+      const int64_t n_row = row ? p.rows : 0, n_col = col ? p.cols : 0;
+      chan_finalize_kernel<<<(unsigned)((n_row + n_col + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+          reinterpret_cast<float*>(p.s_row), n_row, reinterpret_cast<float*>(p.s_col), n_col, p.nonfinite);
+      return hipGetLastError();
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -84,6 +84,8 @@ extern "C" {
 #define FP8MI_BLOCK_1x128 2    /* ROW: 1x128 along cols; COL: 128x1 down rows            */
 #define FP8MI_BLOCK_128x128 3  /* one scale per 128x128 tile                             */
 #define FP8MI_MX_1x32 4        /* ROW: 1x32 along cols; COL: 32x1 down rows; E8M0 bytes  */
+#define FP8MI_CHANNEL 5        /* ROW: one scale per row; COL: one per column [P3 Fig. 1] */
+#define FP8MI_MX_1x32_OCP 6    /* MX_1x32 with the OCP floor rule for the E8M0 exponent */
 
 /* which code layouts to write */
 #define FP8MI_ROW 1         /* q_row [rows x cols]                          */
@@ -95,6 +97,8 @@ extern "C" {
 #define FP8MI_GEMM_BLOCK_1x128_128x128 1 /* s_a [M x ceil(K/128)], s_b [ceil(N/128) x ceil(K/128)] */
 #define FP8MI_GEMM_BLOCK_1x128_1x128 2   /* s_a [M x ceil(K/128)], s_b [N x ceil(K/128)]      */
 #define FP8MI_GEMM_MX_1x32 3             /* s_a [M x ceil(K/32)], s_b [N x ceil(K/32)] E8M0   */
+#define FP8MI_GEMM_BLOCK_128x128_128x128 4 /* s_a [ceil(M/128) x ceil(K/128)], s_b [ceil(N/128) x ceil(K/128)] */
+#define FP8MI_GEMM_CHANNEL 5             /* s_a [M], s_b [N]: one float per row of A and of B  */
 
 /* Slots of a delayed-scaling amax accumulator.  Each workgroup of a
  * TENSOR_DELAYED cast max-accumulates into a slot of its own with plain
@@ -117,6 +121,12 @@ extern "C" {
  *        BLOCK_1x128   s_row = float [rows x ceil(cols/128)]   (s_inv per block)
  *        BLOCK_128x128 s_row = float [ceil(rows/128) x ceil(cols/128)]
  *        MX_1x32       s_row = uint8 [rows x ceil(cols/32)]    (E8M0 bytes)
+ *        MX_1x32_OCP   as MX_1x32; the exponent is floor(log2(amax)) - emax
+ *                      (emax 8 for E4M3, 15 for E5M2) as the OCP microscaling
+ *                      specification computes it, so elements above max
+ *                      saturate; MX_1x32 takes the smallest power of two
+ *                      under which none does.
+ *        CHANNEL       s_row = float [rows]  (s_inv of each whole row)
  *        TENSOR_*      s_row unused.
  *   q_col, ld_q_col, s_col       : COL output.  Codes of x^T, [cols x rows].
  *        BLOCK_1x128   blocks run 128 rows down each column:
@@ -125,6 +135,7 @@ extern "C" {
  *                      s_col = float [ceil(cols/128) x ceil(rows/128)]
  *        MX_1x32       32 rows down each column:
  *                      s_col = uint8 [cols x ceil(rows/32)]
+ *        CHANNEL       s_col = float [cols]  (s_inv of each whole column)
  *        TENSOR_*      same scale as ROW (a plain transpose of the codes).
  *   scale, scale_inv, amax       : per-tensor recipes only (device floats).
  *        CURRENT: writes amax = max|x| (NaN if x holds a NaN), scale and
@@ -138,9 +149,12 @@ extern "C" {
  *                 once; fp8_amax_history_update consumes and re-zeroes it.
  *                 Casts that share an accumulator must be ordered on one
  *                 stream.  scale_inv is not touched.
+ *        CHANNEL: before the cast, the code outputs briefly hold per-tile
+ *                 partial maxima inside their logical bytes and the scale
+ *                 outputs hold the scales s; both are final on completion.
  *   nonfinite                    : optional (may be NULL) device int32; gets
- *        += the number of scale blocks whose amax was NaN/Inf (CURRENT and
- *        block recipes; those blocks use s = 1, MX byte 0xFF).
+ *        += the number of scale blocks whose amax was NaN/Inf (CURRENT,
+ *        channel and block recipes; those blocks use s = 1, MX byte 0xFF).
  * x must not overlap any output.
  * Alignment: x, q_row, q_col 16-byte aligned; ld_x * sizeof(elem),
  * ld_q_row and ld_q_col multiples of 16 bytes.  rows == 0 or cols == 0 is
@@ -186,6 +200,10 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  *   Uses:  fprop  a = X   [M x K], b = W   [N x K];
  *          dgrad  a = dY  [M x N], b = W^T [K x N]  (contraction over N);
  *          wgrad  a = dY^T[N x M], b = X^T [K x M]  (contraction over M).
+ *   BLOCK_128x128_128x128 (both operands in 128x128 tiles) promotes each
+ *   128-deep block with s_a[i / 128][kb] * s_b[j / 128][kb]; CHANNEL
+ *   scales the FP32 result by s_a[i] * s_b[j] (the rows of a and b are the
+ *   channels: a per-row scale of X and a per-output-channel scale of W).
  * Requirements: M, N, K >= 0; K % 16 == 0; a, b 16-byte aligned,
  * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 (else
  * FP8MI_ERR_UNSUPPORTED); ldc >= N.  K == 0 writes zeros.

@@ -98,7 +98,7 @@ def _g(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(fmt_a=3), fm.ERR_ENUM),
     (dict(fmt_b=-1), fm.ERR_ENUM),
-    (dict(recipe=4), fm.ERR_ENUM),
+    (dict(recipe=6), fm.ERR_ENUM),
     (dict(c_dtype=2), fm.ERR_ENUM),
     (dict(M=-1), fm.ERR_SHAPE),
     (dict(c=None), fm.ERR_NULL),

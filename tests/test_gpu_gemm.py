@@ -33,6 +33,16 @@ def _operands(recipe, M, N, K, fa, fb, seed):
         qb, gb, _ = oracle.quantize_blocks(nb, xb, 128, 128)
         da, db = oracle.dequant(na, qa, ga, 1, 128), oracle.dequant(nb, qb, gb, 128, 128)
         sa, sb = dev(ga), dev(gb)
+    elif recipe == fm.GEMM_BLOCK_128x128_128x128:
+        qa, ga, _ = oracle.quantize_blocks(na, xa, 128, 128)
+        qb, gb, _ = oracle.quantize_blocks(nb, xb, 128, 128)
+        da, db = oracle.dequant(na, qa, ga, 128, 128), oracle.dequant(nb, qb, gb, 128, 128)
+        sa, sb = dev(ga), dev(gb)
+    elif recipe == fm.GEMM_CHANNEL:
+        qa, ga, _ = oracle.quantize_channel(na, xa)
+        qb, gb, _ = oracle.quantize_channel(nb, xb)
+        da, db = oracle.dequant(na, qa, ga[:, None], 1, K), oracle.dequant(nb, qb, gb[:, None], 1, K)
+        sa, sb = dev(ga), dev(gb)
     elif recipe == fm.GEMM_BLOCK_1x128_1x128:
         qa, ga, _ = oracle.quantize_blocks(na, xa, 1, 128)
         qb, gb, _ = oracle.quantize_blocks(nb, xb, 1, 128)
@@ -53,7 +63,8 @@ def _check(c, da, db, out):
     assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:5])
 
 
-RECIPES = [fm.GEMM_TENSOR, fm.GEMM_BLOCK_1x128_128x128, fm.GEMM_BLOCK_1x128_1x128, fm.GEMM_MX_1x32]
+RECIPES = [fm.GEMM_TENSOR, fm.GEMM_BLOCK_1x128_128x128, fm.GEMM_BLOCK_1x128_1x128, fm.GEMM_MX_1x32,
+           fm.GEMM_BLOCK_128x128_128x128, fm.GEMM_CHANNEL]
 SHAPES = [(128, 256, 512), (200, 300, 400), (256, 512, 1024), (17, 33, 144), (513, 129, 256)]
 
 
@@ -97,6 +108,14 @@ def test_exact_small_integer_products(recipe):
     if recipe == fm.GEMM_TENSOR:
         ga, gb = np.array([0.5], np.float32), np.array([4.0], np.float32)
         da, db = oracle.dequant("e4m3", qa, ga[0]), oracle.dequant("e5m2", qb, gb[0])
+    elif recipe == fm.GEMM_CHANNEL:
+        ga = (2.0 ** rng.integers(-2, 3, M)).astype(np.float32)
+        gb = (2.0 ** rng.integers(-2, 3, N)).astype(np.float32)
+        da, db = oracle.dequant("e4m3", qa, ga[:, None], 1, K), oracle.dequant("e5m2", qb, gb[:, None], 1, K)
+    elif recipe == fm.GEMM_BLOCK_128x128_128x128:
+        ga = (2.0 ** rng.integers(-2, 3, ((M + 127) // 128, K // 128))).astype(np.float32)
+        gb = (2.0 ** rng.integers(-2, 3, ((N + 127) // 128, K // 128))).astype(np.float32)
+        da, db = oracle.dequant("e4m3", qa, ga, 128, 128), oracle.dequant("e5m2", qb, gb, 128, 128)
     elif recipe == fm.GEMM_MX_1x32:
         ga = rng.integers(125, 130, (M, K // 32)).astype(np.uint8)
         gb = rng.integers(125, 130, (N, K // 32)).astype(np.uint8)

@@ -30,18 +30,21 @@ def _input(rows, cols, seed, dtype, specials=False):
 
 
 def _oracle_blocks(fmt, xf, recipe, orient):
+    """(codes, scales) of one layout; COL codes are those of x^T."""
     if recipe == fm.BLOCK_1x128:
         br, bc = (1, 128) if orient == fm.ROW else (128, 1)
         q, g, _ = oracle.quantize_blocks(fmt, xf, br, bc)
     elif recipe == fm.BLOCK_128x128:
         q, g, _ = oracle.quantize_blocks(fmt, xf, 128, 128)
+    elif recipe == fm.CHANNEL:  # one scale per row (ROW) or per column (COL)
+        return oracle.quantize_channel(fmt, xf if orient == fm.ROW else np.ascontiguousarray(xf.T))[:2]
     else:
         br, bc = (1, 32) if orient == fm.ROW else (32, 1)
-        q, g, _ = oracle.quantize_mx(fmt, xf, br, bc)
+        q, g, _ = oracle.quantize_mx(fmt, xf, br, bc, "floor" if recipe == fm.MX_1x32_OCP else "ceil")
     return (q, g) if orient == fm.ROW else (q.T, g.T)
 
 
-@pytest.mark.parametrize("recipe", [fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32])
+@pytest.mark.parametrize("recipe", [fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32, fm.MX_1x32_OCP, fm.CHANNEL])
 @pytest.mark.parametrize("orient", [fm.ROW, fm.COL, fm.ROW_AND_COL])
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -60,6 +63,22 @@ def test_block_recipes_match_oracle(recipe, orient, fmt, dtype):
             oq, og = _oracle_blocks(name, xf, recipe, fm.COL)
             assert np.array_equal(codes(q.q_col, cols, rows), oq), (rows, cols)
             assert np.array_equal(host(q.s_col), og), (rows, cols)
+
+
+@pytest.mark.parametrize("shape", [(48, 16504), (16500, 24), (257, 136)])
+def test_channel_long_lines_and_margin(shape):
+    """Channel scaling over rows spanning 129 tiles (columns likewise), and
+    with a margin; codes and s_inv of both layouts bit for bit."""
+    need_gpu()
+    rows, cols = shape
+    x = _input(rows, cols, 450, torch.bfloat16)
+    xf = x.float().numpy()
+    for margin in (0, 3):
+        q = fm.quantize(x.cuda(), fm.CHANNEL, fm.E4M3, fm.ROW_AND_COL, margin=margin)
+        oq, og, _ = oracle.quantize_channel("e4m3", xf, margin)
+        assert np.array_equal(codes(q.q_row, rows, cols), oq) and np.array_equal(host(q.s_row), og)
+        oq, og, _ = oracle.quantize_channel("e4m3", np.ascontiguousarray(xf.T), margin)
+        assert np.array_equal(codes(q.q_col, cols, rows), oq) and np.array_equal(host(q.s_col), og)
 
 
 @pytest.mark.parametrize("orient", [fm.ROW, fm.COL, fm.ROW_AND_COL])
@@ -99,7 +118,8 @@ def test_tensor_delayed_matches_oracle(fmt, dtype):
         assert same_f32([acc_amax(amax)], [acc])
 
 
-@pytest.mark.parametrize("recipe", [fm.TENSOR_CURRENT, fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32])
+@pytest.mark.parametrize("recipe", [fm.TENSOR_CURRENT, fm.BLOCK_1x128, fm.BLOCK_128x128, fm.MX_1x32,
+                                    fm.MX_1x32_OCP, fm.CHANNEL])
 def test_nonfinite_inputs(recipe):
     need_gpu()
     rows, cols = 256, 256
@@ -132,8 +152,11 @@ def test_nonfinite_inputs(recipe):
         expected = oracle.quantize_blocks("e4m3", xf, 1, 128)[2] + oracle.quantize_blocks("e4m3", xf, 128, 1)[2]
     elif recipe == fm.BLOCK_128x128:
         expected = oracle.quantize_blocks("e4m3", xf, 128, 128)[2]
+    elif recipe == fm.CHANNEL:
+        expected = oracle.quantize_channel("e4m3", xf)[2] + oracle.quantize_channel("e4m3", xf.T)[2]
     else:
-        expected = oracle.quantize_mx("e4m3", xf, 1, 32)[2] + oracle.quantize_mx("e4m3", xf, 32, 1)[2]
+        rule = "floor" if recipe == fm.MX_1x32_OCP else "ceil"
+        expected = oracle.quantize_mx("e4m3", xf, 1, 32, rule)[2] + oracle.quantize_mx("e4m3", xf, 32, 1, rule)[2]
     assert expected > 0 and host(nf)[0] == expected
 
 

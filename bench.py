@@ -81,9 +81,9 @@ class Step:
         self.qw = torch.empty(N, K, dtype=u8, device=d)
         self.qwt = torch.empty(K, N, dtype=u8, device=d)
         self.qg = torch.empty(M, N, dtype=u8, device=d)
-        f = lambda: torch.zeros(1, dtype=torch.float32, device=d)  # noqa: E731
-        self.sx, self.six, self.ax = f(), f(), f()
-        self.sw, self.siw, self.aw = f(), f(), f()
+        f = lambda n=1: torch.zeros(n, dtype=torch.float32, device=d)  # noqa: E731
+        self.sx, self.six, self.ax = f(), f(), f(fm.AMAX_SLOTS)
+        self.sw, self.siw, self.aw = f(), f(), f(fm.AMAX_SLOTS)
         self.state = fm.DelayedState(fm.E5M2, 200, 0, d)
         self.y = torch.empty(M, N, dtype=torch.bfloat16, device=d)
         self.dx = torch.empty(M, K, dtype=torch.bfloat16, device=d)

@@ -33,7 +33,7 @@ CHANNEL, MX_1x32_OCP = 5, 6
 ROW, COL, ROW_AND_COL = 1, 2, 3
 GEMM_TENSOR, GEMM_BLOCK_1x128_128x128, GEMM_BLOCK_1x128_1x128, GEMM_MX_1x32 = 0, 1, 2, 3
 GEMM_BLOCK_128x128_128x128, GEMM_CHANNEL = 4, 5
-AMAX_SLOTS = 1024  # floats in a delayed-scaling amax accumulator
+AMAX_SLOTS = 1024  # floats in the amax array of a per-tensor cast
 
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
 TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
@@ -201,9 +201,9 @@ def quantize(x: torch.Tensor, recipe: int, fmt: int, orient: int = ROW, margin: 
         if recipe == TENSOR_CURRENT:  # delayed leaves scale_inv to the history update
             out.scale_inv = torch.empty(1, dtype=torch.float32, device=dev)
         if amax is None:
-            amax = torch.zeros(AMAX_SLOTS if recipe == TENSOR_DELAYED else 1, dtype=torch.float32, device=dev)
-        if recipe == TENSOR_DELAYED and amax.numel() < AMAX_SLOTS:
-            raise Fp8Error(f"a delayed-scaling amax accumulator holds {AMAX_SLOTS} floats")
+            amax = torch.zeros(AMAX_SLOTS, dtype=torch.float32, device=dev)
+        if amax.numel() < AMAX_SLOTS:
+            raise Fp8Error(f"the amax array of a per-tensor cast holds {AMAX_SLOTS} floats")
         out.amax = amax
     out.nonfinite = nonfinite
     st = fp8_quantize(x, x_dtype, rows, cols, x.stride(0), recipe, fmt, orient, margin,

@@ -150,6 +150,6 @@ const char* fp8_status_string(int status) {
   return "unknown status";
 }
 
-int fp8_version(void) { return 300; }
+int fp8_version(void) { return 400; }
 
 }  // extern "C"

@@ -21,8 +21,10 @@
 //     thread walks a column pair for 32 rows, and the codes go back through
 //     LDS so that each output row leaves as whole 128-byte lines.
 // Per-tensor current scaling needs the amax of the whole tensor before any
-// cast: a reduction pass leaves one partial maximum per workgroup, a
-// one-workgroup pass folds them into *amax, then the cast runs.  No kernel
+// cast: a reduction pass leaves one partial maximum per workgroup in the
+// caller's amax array, and every workgroup of the cast folds those few
+// partials itself before its first tile (workgroup 0 stores the result in
+// amax[0]), so no launch is spent on the fold.  No kernel
 // combines results across workgroups with atomics: on MI355X atomics on one
 // address serialise (about 14 ns each), which for a thousand workgroups
 // costs as much as the whole cast.
@@ -165,9 +167,10 @@ struct TileArgs {
   void* s_col;
   float* scale;       // per-tensor: in (delayed) / out (current)
   float* scale_inv;   // per-tensor current: out
-  float* amax;        // per-tensor: in (current) / slot accumulator (delayed)
+  float* amax;        // per-tensor: out amax[0] + partial slots amax[1..] (current) / slot accumulator (delayed)
   int32_t* nonfinite;
   int margin;
+  int nparts;         // current: partial maxima in amax[1 .. nparts]
 };
 
 // max |x| key of 8 BF16 values packed in a uint4: packed 16-bit max of the
@@ -267,15 +270,29 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
   const int64_t tiles_x = (a.cols + kTile - 1) / kTile;
   const int64_t tiles = tiles_x * ((a.rows + kTile - 1) / kTile);
 
+  // the first tile's words are in flight while the scale is worked out
+  Raw<InT> cur, nxt;
+  int64_t t = blockIdx.x;
+  if (t < tiles) {
+    const int64_t by = t / tiles_x, bx = t - by * tiles_x;
+    cur.load(x, a.ld_x, a.rows, by * kTile + g, bx * kTile + 8 * li, a.cols - (bx * kTile + 8 * li));
+  }
+
   // ---- per-tensor scale (the same for every tile)
   float s_tensor = 1.0f;
   bool safe_tensor = true;
   if constexpr (MODE == MODE_TENSOR) {
     if constexpr (CURRENT) {
-      const float am = *a.amax;
+      // every workgroup folds the amax pass's partial maxima (a few KB, from
+      // L2); none of them writes the slots, so there is no ordering to keep
+      const uint32_t* slots = reinterpret_cast<const uint32_t*>(a.amax) + 1;
+      uint32_t k = 0;
+      for (int i = tid; i < a.nparts; i += kThreads) k = k > slots[i] ? k : slots[i];
+      const float am = key_to_float(wg_max_u32(k, red4));
       s_tensor = scale_from_amax<FMT>(am, a.margin);
       safe_tensor = !is_finite(am);
       if (blockIdx.x == 0 && tid == 0) {
+        *a.amax = am;
         *a.scale = s_tensor;
         *a.scale_inv = recip_rn(s_tensor);
         if (safe_tensor && a.nonfinite) atomicAdd(a.nonfinite, 1);
@@ -292,12 +309,6 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
     if (tid == 0) amax_acc = reinterpret_cast<const uint32_t*>(a.amax)[blockIdx.x];
   }
 
-  Raw<InT> cur, nxt;
-  int64_t t = blockIdx.x;
-  if (t < tiles) {
-    const int64_t by = t / tiles_x, bx = t - by * tiles_x;
-    cur.load(x, a.ld_x, a.rows, by * kTile + g, bx * kTile + 8 * li, a.cols - (bx * kTile + 8 * li));
-  }
   for (; t < tiles; t += gridDim.x) {
     const int64_t by = t / tiles_x, bx = t - by * tiles_x;
     const int64_t tn = t + gridDim.x;
@@ -537,25 +548,11 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
 // ---------------------------------------------------------------------------
 // Per-tensor amax for current scaling: max |x| over the tensor, NaN-dominant.
 // Each workgroup of the reduction pass stores its partial maximum (a |x| bit
-// pattern) in a 4-byte slot laid over the code output, which the cast pass
-// overwrites afterwards: slot p sits in output row p / per_row at byte
-// 4 (p % per_row).  A single-workgroup pass stores straight to *amax.
+// pattern) in slot 1 + w of the caller's amax array; every workgroup of the
+// cast pass folds the slots itself and workgroup 0 writes amax[0].
 // ---------------------------------------------------------------------------
-struct Slots {
-  uint8_t* base;
-  int64_t ld;       // bytes between output rows
-  int64_t per_row;  // slots per output row (row length / 4)
-  __device__ __forceinline__ uint32_t* at(int64_t p) const {
-    return reinterpret_cast<uint32_t*>(base + (p / per_row) * ld + 4 * (p % per_row));
-  }
-};
-
-__device__ __forceinline__ void put_partial(uint32_t k, const Slots& sl, float* amax) {
-  const int64_t p = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  if (gridDim.x * gridDim.y == 1)
-    *reinterpret_cast<uint32_t*>(amax) = k;
-  else
-    *sl.at(p) = k;
+__device__ __forceinline__ void put_partial(uint32_t k, uint32_t* slots) {
+  slots[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = k;
 }
 
 // max |x| key of 8 consecutive elements (fewer at a ragged row end)
@@ -575,7 +572,7 @@ __device__ __forceinline__ uint32_t chunk_key(const float* p, int64_t n) {
 // blockIdx.x * 256 + tid; four rows per trip keep four loads in flight.
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* x, int64_t rows, int64_t cols,
-                                                        int64_t ld, Slots sl, float* amax) {
+                                                        int64_t ld, uint32_t* slots) {
   __shared__ uint32_t red4[4];
   const int64_t cpr = (cols + 7) / 8;
   uint32_t k = 0;
@@ -597,13 +594,13 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const InT* x, int64_t ro
     }
   }
   k = wg_max_u32(k, red4);
-  if (threadIdx.x == 0) put_partial(k, sl, amax);
+  if (threadIdx.x == 0) put_partial(k, slots);
 }
 
 // Contiguous tensors (ld == cols): one flat stream of 8-element chunks,
 // grid-strided with four independent 16-byte loads per trip.
 template <typename InT>
-__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64_t n, Slots sl, float* amax) {
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64_t n, uint32_t* slots) {
   __shared__ uint32_t red4[4];
   const int64_t nch = n / 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -627,25 +624,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const InT* x, int64
     k = k > m ? k : m;
   }
   k = wg_max_u32(k, red4);
-  if (threadIdx.x == 0) put_partial(k, sl, amax);
-}
-
-// One workgroup of 1024 threads: *amax = max over the `count` (<= 2048)
-// partial slots, all loads issued up front.
-constexpr int kFinThreads = 1024;
-__global__ __launch_bounds__(kFinThreads) void amax_finalize_kernel(Slots sl, int count, float* amax) {
-  __shared__ uint32_t red[kFinThreads / 64];
-  const int t = threadIdx.x;
-  const uint32_t v0 = t < count ? *sl.at(t) : 0u;
-  const uint32_t v1 = t + kFinThreads < count ? *sl.at(t + kFinThreads) : 0u;
-  uint32_t k = group_max_u32<64>(v0 > v1 ? v0 : v1);
-  if ((t & 63) == 0) red[t >> 6] = k;
-  __syncthreads();
-  if (t == 0) {
-#pragma unroll
-    for (int w = 0; w < kFinThreads / 64; ++w) k = k > red[w] ? k : red[w];
-    *reinterpret_cast<uint32_t*>(amax) = k;
-  }
+  if (threadIdx.x == 0) put_partial(k, slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,9 +757,9 @@ hipError_t launch_tile_k(const TileArgs& a, int64_t tiles, hipStream_t st) {
 }
 
 template <typename InT, int FMT, int MODE, bool CURRENT>
-hipError_t launch_tile(const QuantParams& p, hipStream_t st) {
+hipError_t launch_tile(const QuantParams& p, hipStream_t st, int nparts = 0) {
   TileArgs a{p.x, p.rows, p.cols, p.ld_x, p.q_row, p.ld_q_row, p.s_row, p.q_col, p.ld_q_col,
-             p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin};
+             p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin, nparts};
   const int64_t tiles = ((p.cols + kTile - 1) / kTile) * ((p.rows + kTile - 1) / kTile);
   const bool row = p.orient & 1, col = p.orient & 2;
   if (row && col) return launch_tile_k<InT, FMT, MODE, true, true, CURRENT>(a, tiles, st);
@@ -794,21 +773,16 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
     case kRecipeTensorCurrent: {
       if (p.rows > 0 && p.cols > 0) {
         const InT* x = reinterpret_cast<const InT*>(p.x);
-        // partial-maximum slots over the first code output
-        const bool row = p.orient & 1;
-        Slots sl{row ? p.q_row : p.q_col, row ? p.ld_q_row : p.ld_q_col, (row ? p.cols : p.rows) / 4};
-        const int64_t cap_slots = sl.per_row * (row ? p.rows : p.cols);
+        uint32_t* slots = reinterpret_cast<uint32_t*>(p.amax) + 1;  // amax[1 .. kAmaxSlots - 1]
         int64_t cap = (int64_t)cu_count() * 8;
-        cap = cap < 2 * kFinThreads ? cap : 2 * kFinThreads;  // what the finalize pass folds
-        cap = cap < cap_slots ? cap : cap_slots;
-        cap = cap > 1 ? cap : 1;
+        cap = cap < kAmaxSlots - 1 ? cap : kAmaxSlots - 1;
         int64_t parts;
         if (p.ld_x == p.cols || p.rows == 1) {
           const int64_t n = p.rows * p.cols;
           int64_t blocks = (n / 8 + kThreads - 1) / kThreads;
           blocks = blocks < cap ? blocks : cap;
           parts = blocks > 0 ? blocks : 1;
-          amax_flat_kernel<InT><<<(unsigned)parts, kThreads, 0, st>>>(x, n, sl, p.amax);
+          amax_flat_kernel<InT><<<(unsigned)parts, kThreads, 0, st>>>(x, n, slots);
         } else {
           const int64_t cpr = (p.cols + 7) / 8;
           int64_t gx = (cpr + kThreads - 1) / kThreads;
@@ -820,10 +794,9 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
           gy = gy > 0 ? gy : 1;
           parts = gx * gy;
           amax_kernel<InT><<<dim3((unsigned)gx, (unsigned)gy), kThreads, 0, st>>>(x, p.rows, p.cols, p.ld_x,
-                                                                                  sl, p.amax);
+                                                                                  slots);
         }
-        if (parts > 1) amax_finalize_kernel<<<1, kFinThreads, 0, st>>>(sl, (int)parts, p.amax);
-        return launch_tile<InT, FMT, MODE_TENSOR, true>(p, st);
+        return launch_tile<InT, FMT, MODE_TENSOR, true>(p, st, (int)parts);
       }
       // empty tensor: amax = 0 -> scale = scale_inv = 1
       return launch_empty_scale(p.amax, p.scale, p.scale_inv, st);
@@ -841,7 +814,7 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
       return launch_tile<InT, FMT, MODE_MX32F, false>(p, st);
     case kRecipeChannel: {
       TileArgs a{p.x, p.rows, p.cols, p.ld_x, p.q_row, p.ld_q_row, p.s_row, p.q_col, p.ld_q_col,
-                 p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin};
+                 p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin, 0};
       const bool row = p.orient & 1, col = p.orient & 2;
       const int64_t tx = (p.cols + kTile - 1) / kTile, ty = (p.rows + kTile - 1) / kTile;
       const unsigned tiles = (unsigned)(tx * ty);

@@ -78,7 +78,8 @@ extern "C" {
 #define FP8MI_OUT_FP32 1
 
 /* quantize recipes [P1 sec. 2.1-2.3] */
-#define FP8MI_TENSOR_CURRENT 0 /* amax of x now -> s; writes amax, scale, scale_inv    */
+#define FP8MI_TENSOR_CURRENT 0 /* amax of x now -> s; writes amax[0], scale, scale_inv */
+                               /* (amax: float[FP8MI_AMAX_SLOTS], the rest scratch)     */
 #define FP8MI_TENSOR_DELAYED 1 /* cast with *scale; max-accumulates max|x| into the     */
                                /* amax accumulator float[FP8MI_AMAX_SLOTS]             */
 #define FP8MI_BLOCK_1x128 2    /* ROW: 1x128 along cols; COL: 128x1 down rows            */
@@ -100,11 +101,13 @@ extern "C" {
 #define FP8MI_GEMM_BLOCK_128x128_128x128 4 /* s_a [ceil(M/128) x ceil(K/128)], s_b [ceil(N/128) x ceil(K/128)] */
 #define FP8MI_GEMM_CHANNEL 5             /* s_a [M], s_b [N]: one float per row of A and of B  */
 
-/* Slots of a delayed-scaling amax accumulator.  Each workgroup of a
+/* Floats in the amax array of a per-tensor cast.  Each workgroup of a
  * TENSOR_DELAYED cast max-accumulates into a slot of its own with plain
- * loads and stores; fp8_amax_history_update folds the slots into the step's
- * amax.  (Atomics on one address serialise on MI355X; with a thousand
- * workgroups they would cost as much as the cast itself.) */
+ * loads and stores, and fp8_amax_history_update folds the slots into the
+ * step's amax; a TENSOR_CURRENT cast keeps its per-workgroup partial maxima
+ * in slots 1.. and the result in slot 0.  (Atomics on one address serialise
+ * on MI355X; with a thousand workgroups they would cost as much as the cast
+ * itself.) */
 #define FP8MI_AMAX_SLOTS 1024
 
 /* ---- entry points ----------------------------------------------------- */
@@ -138,10 +141,10 @@ extern "C" {
  *        CHANNEL       s_col = float [cols]  (s_inv of each whole column)
  *        TENSOR_*      same scale as ROW (a plain transpose of the codes).
  *   scale, scale_inv, amax       : per-tensor recipes only (device floats).
- *        CURRENT: writes amax = max|x| (NaN if x holds a NaN), scale and
- *                 scale_inv.  Before the cast, the first code output (q_row,
- *                 else q_col) briefly holds per-workgroup partial maxima
- *                 inside its [rows x cols] (resp. [cols x rows]) bytes.
+ *        CURRENT: amax is float[FP8MI_AMAX_SLOTS]: amax[0] receives
+ *                 max|x| (NaN if x holds a NaN); amax[1..] is scratch for
+ *                 per-workgroup partial maxima (left holding them).  Writes
+ *                 scale and scale_inv.
  *        DELAYED: reads *scale; amax is the accumulator
  *                 float[FP8MI_AMAX_SLOTS]: the step's amax is the largest
  *                 slot (NaN-dominant, comparing |x| bit patterns) and a cast

@@ -6,6 +6,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import fp8_scaled_quantization_scale_amd as fm
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (fp8_\w+)$", out, flags=re.M))
     assert set(_declared()) <= exported
-    assert fm.version() == 300
+    assert fm.version() == 400
     assert fm.status_string(fm.ERR_ALIGN).startswith("pointer")
 
 
@@ -154,3 +155,13 @@ def test_bf16_gemm_validation(kw, code):
 def test_bf16_gemm_empty_is_ok_without_launch():
     assert _b(M=0) == fm.OK
     assert _b(N=0, c=None) == fm.OK
+
+
+def test_binding_rejects_a_short_amax_array():
+    """Per-tensor casts take an amax array of AMAX_SLOTS floats (current
+    scaling keeps its partial maxima there); the binding refuses a shorter
+    one before any library call."""
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    for recipe in (fm.TENSOR_CURRENT, fm.TENSOR_DELAYED):
+        with pytest.raises(fm.Fp8Error, match="amax"):
+            fm.quantize(x, recipe, fm.E4M3, fm.ROW, scale=torch.ones(1), amax=torch.zeros(1))

@@ -120,7 +120,7 @@ def test_fullsize_tensor_llama3_8b_attn():
                                       ("W", W, st.qw, st.sw, st.siw, st.aw, st.qwt)):
         a = oracle.amax(t.float().cpu().numpy())
         os_, osi, _ = oracle.scale_from_amax("e4m3", a)
-        assert same_f32(host(am), [a]) and same_f32(host(s), [os_]) and same_f32(host(si), [osi]), name
+        assert same_f32(host(am)[:1], [a]) and same_f32(host(s), [os_]) and same_f32(host(si), [osi]), name
         scales[name] = (os_, osi)
         r = pick(t.shape[0], 24, 3)
         oq, _ = oracle.quantize_delayed("e4m3", rows_f32(t, r), os_)

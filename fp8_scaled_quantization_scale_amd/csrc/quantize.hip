@@ -347,6 +347,34 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
 
     // ---- ROW layout, straight from registers
     if constexpr (ROW) {
+      // 1x128: the 16 lanes of a group hold the same 8 row maxima; lane li
+      // derives the scale of row li % 8 (one correctly rounded divide pair
+      // per lane instead of eight) and the group reads them back by shuffle
+      float s_rows[8];
+      bool bad_rows[8];
+      if constexpr (MODE == MODE_B1x128) {
+        uint32_t kk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float v[8];
+          cur.row(i, v);
+          kk[i] = group_max_u32<16>(cur.key(i, v));
+          bad_rows[i] = !is_finite(key_to_float(kk[i]));
+        }
+        uint32_t kj = kk[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) kj = ((li & 7) == j) ? kk[j] : kj;
+        const float amj = key_to_float(kj);
+        const float sj = scale_from_amax<FMT>(amj, a.margin);
+        const int64_t rj = row0 + g + 16 * (li & 7);
+        if (li < 8 && rj < a.rows) {
+          reinterpret_cast<float*>(a.s_row)[rj * tiles_x + bx] = recip_rn(sj);
+          if (!is_finite(amj) && a.nonfinite) atomicAdd(a.nonfinite, 1);
+        }
+        const int gbase = (tid & 63) & ~15;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_rows[i] = __shfl(sj, gbase + i, 64);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t r = row0 + g + 16 * i;
@@ -355,14 +383,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
         float s = s_t;
         bool safe = safe_t;
         if constexpr (MODE == MODE_B1x128) {
-          const uint32_t k = group_max_u32<16>(cur.key(i, v));
-          const float am = key_to_float(k);
-          s = scale_from_amax<FMT>(am, a.margin);
-          safe = !is_finite(am);
-          if (li == 0 && r < a.rows) {
-            reinterpret_cast<float*>(a.s_row)[r * tiles_x + bx] = recip_rn(s);
-            if (safe && a.nonfinite) atomicAdd(a.nonfinite, 1);
-          }
+          s = s_rows[i];
+          safe = bad_rows[i];
         } else if constexpr (MODE == MODE_MX32 || MODE == MODE_MX32F) {
           const uint32_t k = group_max_u32<4>(cur.key(i, v));
           const int byte = mx_byte<MODE, FMT>(key_to_float(k));

@@ -24,6 +24,10 @@ Recipes (the objects the guide's sec. 2.1-2.2 examples pass to
 * ``MXFP8BlockScaling`` -- 1x32 blocks with E8M0 scales for every operand
   along every contraction dimension (guide sec. 2.3, strategy 4).  The guide
   prints no class name for it; this one follows the other two.
+* ``Float8ChannelScaling`` -- one scale per channel: per token row of X and
+  dY, per output channel of W, and for each backward GEMM per channel of the
+  transposed operand ("Mastering FP8 LLM training", Fig. 1 discussion of
+  channel-wise scaling).  Name chosen here; the pages print none.
 
 ``Format.HYBRID`` puts activations and weights in E4M3 and gradients in E5M2
 (guide sec. 2.1 hybrid format; "FP8 training support", "Why FP8?").  The
@@ -39,9 +43,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (BLOCK_1x128, BLOCK_128x128, COL, E4M3, E5M2, GEMM_BLOCK_1x128_1x128,
-               GEMM_BLOCK_1x128_128x128, GEMM_MX_1x32, GEMM_TENSOR, MX_1x32, ROW, TENSOR_CURRENT,
-               TENSOR_DELAYED, DelayedState, Fp8Error, gemm, load, quantize)
+from . import (BLOCK_1x128, BLOCK_128x128, CHANNEL, COL, E4M3, E5M2, GEMM_BLOCK_1x128_1x128,
+               GEMM_BLOCK_1x128_128x128, GEMM_CHANNEL, GEMM_MX_1x32, GEMM_TENSOR, MX_1x32, ROW,
+               TENSOR_CURRENT, TENSOR_DELAYED, DelayedState, Fp8Error, gemm, load, quantize)
 
 
 class Format(enum.Enum):
@@ -74,7 +78,13 @@ class MXFP8BlockScaling:
     fp8_format: Format = Format.E4M3
 
 
-RECIPES = (DelayedScaling, Float8CurrentScaling, Float8BlockScaling, MXFP8BlockScaling)
+@dataclass(frozen=True)
+class Float8ChannelScaling:
+    fp8_format: Format = Format.E4M3
+    margin: int = 0
+
+
+RECIPES = (DelayedScaling, Float8CurrentScaling, Float8BlockScaling, MXFP8BlockScaling, Float8ChannelScaling)
 ROLES = ("x", "w", "g")  # input activation, weight, output gradient
 
 
@@ -110,6 +120,11 @@ def plan(recipe) -> Plan:
             raise Fp8Error("interval must be >= 1 and amax_history_len in [1, 65536]")
         return Plan({"x": (q, fwd), "w": (q, fwd), "g": (q, bwd)},
                     {"fprop": GEMM_TENSOR, "dgrad": GEMM_TENSOR, "wgrad": GEMM_TENSOR}, recipe.margin)
+    if isinstance(recipe, Float8ChannelScaling):
+        if not 0 <= recipe.margin <= 64:
+            raise Fp8Error("margin must be in [0, 64]")
+        return Plan({"x": (CHANNEL, fwd), "w": (CHANNEL, fwd), "g": (CHANNEL, bwd)},
+                    {"fprop": GEMM_CHANNEL, "dgrad": GEMM_CHANNEL, "wgrad": GEMM_CHANNEL}, recipe.margin)
     if isinstance(recipe, Float8BlockScaling):
         return Plan({"x": (BLOCK_1x128, fwd), "w": (BLOCK_128x128, fwd), "g": (BLOCK_1x128, bwd)},
                     {"fprop": GEMM_BLOCK_1x128_128x128, "dgrad": GEMM_BLOCK_1x128_128x128,

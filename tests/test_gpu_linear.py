@@ -46,6 +46,9 @@ class OracleRole:
         if self.rec == fm.TENSOR_DELAYED:
             q, _ = oracle.quantize_delayed(f, x, s)
             return oracle.dequant(f, q, np.float32(1.0) / np.float32(s))
+        if self.rec == fm.CHANNEL:
+            q, si, _ = oracle.quantize_channel(f, x)
+            return oracle.dequant(f, q, si[:, None], 1, x.shape[1])
         if self.rec == fm.MX_1x32:
             q, g, _ = oracle.quantize_mx(f, x, 1, 32)
             return oracle.dequant_mx(f, q, g, 1, 32)
@@ -90,7 +93,8 @@ def _step(lin, x, g):
 
 RECIPES = {"current": fl.Float8CurrentScaling(), "block": fl.Float8BlockScaling(),
            "mx": fl.MXFP8BlockScaling(), "block_hybrid": fl.Float8BlockScaling(fl.Format.HYBRID),
-           "mx_hybrid": fl.MXFP8BlockScaling(fl.Format.HYBRID)}
+           "mx_hybrid": fl.MXFP8BlockScaling(fl.Format.HYBRID), "channel": fl.Float8ChannelScaling(),
+           "channel_hybrid": fl.Float8ChannelScaling(fl.Format.HYBRID)}
 
 
 @pytest.mark.parametrize("name", list(RECIPES))

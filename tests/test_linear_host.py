@@ -21,6 +21,9 @@ def test_plan_per_recipe():
                        "g": (fm.BLOCK_1x128, fm.E4M3)}
     assert p.gemm == {"fprop": fm.GEMM_BLOCK_1x128_128x128, "dgrad": fm.GEMM_BLOCK_1x128_128x128,
                       "wgrad": fm.GEMM_BLOCK_1x128_1x128}
+    p = fl.plan(fl.Float8ChannelScaling(margin=1))
+    assert set(p.quant.values()) == {(fm.CHANNEL, fm.E4M3)} and p.margin == 1
+    assert set(p.gemm.values()) == {fm.GEMM_CHANNEL}
     p = fl.plan(fl.MXFP8BlockScaling(fp8_format=fl.Format.HYBRID))
     assert p.quant["x"] == (fm.MX_1x32, fm.E4M3) and p.quant["g"] == (fm.MX_1x32, fm.E5M2)
     assert set(p.gemm.values()) == {fm.GEMM_MX_1x32}

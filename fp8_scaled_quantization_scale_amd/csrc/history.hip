@@ -28,8 +28,11 @@ __global__ __launch_bounds__(kHistThreads) void history_kernel(float* ring, int3
                                                                int32_t* nonfinite) {
   __shared__ uint32_t redk[kHistThreads / 64];
   __shared__ float redr[kHistThreads / 64];
+  __shared__ float ring_h;
   uint32_t* slots = reinterpret_cast<uint32_t*>(amax);
   const int t = threadIdx.x;
+  // head, slots and ring are all loaded in one round (no load waits on
+  // another); the entry at head is picked out afterwards
   const int h = *head;
   // the step's amax: NaN-dominant max over the slots (|x| bit patterns)
   uint32_t k = 0;
@@ -38,8 +41,11 @@ __global__ __launch_bounds__(kHistThreads) void history_kernel(float* ring, int3
     k = k > v ? k : v;
   }
   float m = 0.0f;  // ring entries are finite and non-negative
-  for (int i = t; i < len; i += kHistThreads)
-    if (i != h) m = fmaxf(m, ring[i]);
+  for (int i = t; i < len; i += kHistThreads) {
+    const float r = ring[i];
+    if (i != h) m = fmaxf(m, r);
+    else ring_h = r;
+  }
   k = group_max_u32<64>(k);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -47,7 +53,6 @@ __global__ __launch_bounds__(kHistThreads) void history_kernel(float* ring, int3
     redk[t >> 6] = k;
     redr[t >> 6] = m;
   }
-  const float ring_h = ring[h];
   __syncthreads();  // every slot and ring entry has been read before they are rewritten
   for (int i = t; i < kAmaxSlots; i += kHistThreads) slots[i] = 0u;
   if (t == 0) {

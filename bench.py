@@ -499,7 +499,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the quantize + GEMM path runs on one GPU's share, see DESIGN.md on sharding)",
+              "(the quantize + GEMM path runs on one GPU's share)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -26,7 +26,7 @@
  *        "Why FP8?" (E4M3 ~400 range for weights/activations, E5M2 for
  *        gradients, dynamic scaling maps the FP32 range onto FP8).
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - E4M3 is OCP E4M3FN (max 448, subnormals, no Inf, NaN = S.1111.111);
  *     E5M2 is OCP E5M2 (max 57344, subnormals, Inf = S.11111.00).
  *   - Encoding is round-to-nearest, ties to the even code, saturating:

@@ -253,7 +253,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   // ---- scales: fetched with range-checked buffer loads (zero past the matrix)
   // into VGPRs before a step's tile DMAs, written to LDS at the end of the
   // iteration; every lane issues the same count so vmcnt stays uniform
-  uint32_t rs[SLW > 0 ? SLW : 1];
+  // scale words of SB consecutive K steps (see load_scales)
+  constexpr int SB = (REC == kGemmBlock1x128) ? 1 : (REC == kGemmMx ? 8 : 4);
+  uint32_t rs[SLW > 0 ? SLW : 1][SB];
   __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
   int nkb = 0;
   if constexpr (kBlock) {
@@ -278,6 +280,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   // A words come first and fill whole waves, so each wave reads one matrix's
   // scales through one (scalar) buffer resource
   static_assert(SA_W % 64 == 0, "A scale words end on a wave boundary");
+  // A step's scale word of a row is 4 bytes, and the rows of a panel lie
+  // nkb words (bytes for MX) apart, so a per-step fetch is one small request
+  // per row.  Where each row's words split evenly into groups of SB steps,
+  // 16-byte fetches bring SB steps at once and the words wait in registers,
+  // moving down one slot per step (MX GEMMs +5-8%; 1x128 x 1x128 keeps one
+  // step per fetch: it has no registers to spare).
+  const bool batched = SB > 1 && (kBlock ? (nkb % SB == 0) : (nkb % (4 * SB) == 0));
   auto load_scales = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < SLW; ++i) {
@@ -285,13 +294,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
       const bool isa = 64 * wave + NTHR * i < SA_W;  // wave-uniform
       const int r = isa ? t : t - SA_W;  // row (or 128-row tile) within the panel
       const __amdgpu_buffer_rsrc_t rsrc = isa ? rsa : rsb;
+      if constexpr (SB > 1) {
+        if (batched) {
+          if (kt % SB == 0) {  // steps kt .. kt + SB - 1, inside the row
+            const uint32_t off = (t < S_W) ? (uint32_t)(kBlock ? (r * nkb + kt) * 4 : r * nkb + 4 * kt) : kOOB;
+            typedef int v4i __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int h = 0; h < SB / 4; ++h) {
+              const v4i w = __builtin_bit_cast(
+                  v4i, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off == kOOB ? kOOB : off + 16 * h, 0, 0));
+#pragma unroll
+              for (int q = 0; q < 4; ++q) rs[i][4 * h + q] = (uint32_t)w[q];
+            }
+          }
+          continue;
+        }
+      }
       if constexpr (kBlock) {
         const uint32_t off = (t < S_W) ? (uint32_t)((r * nkb + kt) * 4) : kOOB;
-        rs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+        rs[i][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
       } else if constexpr (REC == kGemmMx) {
         if ((nkb & 3) == 0) {  // the step's 4 bytes are one aligned dword
           const uint32_t off = (t < S_W) ? (uint32_t)(r * nkb + 4 * kt) : kOOB;
-          rs[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+          rs[i][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
         } else {
           uint32_t w = 0;
 #pragma unroll
@@ -300,7 +325,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
             const uint32_t off = (t < S_W && kb < nkb) ? (uint32_t)(r * nkb + kb) : kOOB;
             w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsrc, off, 0, 0) << (8 * j);
           }
-          rs[i] = w;
+          rs[i][0] = w;
         }
       }
     }
@@ -329,12 +354,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
         const int base = isa ? mx_pos_a(t) : 4 * BM + mx_pos_b(t - SA_W);
         const int gstride = isa ? BM : BN;
         uint8_t* dst = sbytes[kt % STAGES] + base;
-        const uint32_t w = rs[i];
+        const uint32_t w = rs[i][0];
 #pragma unroll
         for (int g = 0; g < 4; ++g) dst[g * gstride] = (uint8_t)(w >> (8 * g));
       } else {
-        sscale[kt % STAGES][t] = rs[i];  // branch-free: keeps the K step one scheduling region
+        sscale[kt % STAGES][t] = rs[i][0];  // branch-free: keeps the K step one scheduling region
       }
+      // the next step's word moves to slot 0 (a per-step fetch refills it)
+#pragma unroll
+      for (int q = 0; q + 1 < (int)(sizeof(rs[i]) / sizeof(rs[i][0])); ++q) rs[i][q] = rs[i][q + 1];
     }
   };
 

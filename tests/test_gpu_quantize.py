@@ -307,3 +307,47 @@ def test_every_in_range_fp32_input_fast_path(fmt):
             bad += int((got != parallel_encode(name, v)).sum())
             del x, q
     assert bad == 0
+
+
+@pytest.mark.parametrize("dtype,shape,orient", [
+    (torch.bfloat16, (8192, 4096), fm.ROW),          # 1023 partial maxima, every slot of the amax array
+    (torch.bfloat16, (4096, 4096), fm.ROW_AND_COL),
+    (torch.bfloat16, (8192, 6400), fm.ROW),
+    (torch.bfloat16, (8192, 4096), fm.ROW_AND_COL),
+    (torch.float32, (2048, 4096), fm.ROW),
+    (torch.float32, (4096, 6144), fm.ROW),
+])
+def test_tensor_current_large(dtype, shape, orient):
+    """Current scaling at layer sizes, where the amax pass leaves the most
+    partial maxima and the cast folds them all, with the largest magnitude in
+    the last tile: codes, scale and amax bit for bit against the oracle."""
+    need_gpu()
+    rows, cols = shape
+    x = _input(rows, cols, 300 + rows // 64 + cols, dtype)
+    x[rows - 1, cols - 1] = 3.0e4  # the largest magnitude sits in the last tile
+    q = fm.quantize(x.cuda(), fm.TENSOR_CURRENT, fm.E4M3, orient)
+    oq, s, si_, am, _ = oracle.quantize_current("e4m3", x.float().numpy())
+    assert same_f32(host(q.amax)[:1], [am])
+    assert same_f32(host(q.scale), [s]) and same_f32(host(q.scale_inv), [si_])
+    if orient & fm.ROW:
+        assert np.array_equal(codes(q.q_row, rows, cols), oq)
+    if orient & fm.COL:
+        assert np.array_equal(codes(q.q_col, cols, rows), oq.T)
+
+
+def test_tensor_current_reused_amax_array():
+    """Consecutive current-scaling casts sharing one amax array, large and
+    small: each sees only its own tensor's maxima (partials left by an
+    earlier, larger call never count)."""
+    need_gpu()
+    am = torch.zeros(fm.AMAX_SLOTS, dtype=torch.float32, device="cuda")
+    for i, (rows, cols, peak) in enumerate([(4096, 4096, 900.0), (256, 384, 2.0), (8192, 6400, 40.0),
+                                            (384, 256, 0.5), (4096, 4096, 7.0), (2, 8, 0.25)]):
+        x = (_input(rows, cols, 400 + i, torch.bfloat16) * 0.001).to(torch.bfloat16)
+        x[rows // 2, cols // 2] = peak
+        q = fm.quantize(x.cuda(), fm.TENSOR_CURRENT, fm.E4M3, fm.ROW, amax=am)
+        oq, s, si_, a, _ = oracle.quantize_current("e4m3", x.float().numpy())
+        assert same_f32(host(am)[:1], [a]) and a == peak
+        assert same_f32(host(q.scale), [s])
+        assert np.array_equal(codes(q.q_row, rows, cols), oq)
+

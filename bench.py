@@ -18,7 +18,10 @@ timed steps with HIP events on the stream it runs on, in every 4th step
 (--event-every).  The events are created without the system-scope release
 fence (a fenced event writes back and invalidates the caches and stalls the
 queue for several microseconds); even so each record costs the queue about
-4.5 us, which is why not every step carries them.  "cpu_baseline" is the CPU oracle timed on a
+4.5 us, which is why not every step carries them.  "hbm_copy" is a 1 GiB
+device copy timed on the same GPU: each cast's "frac_copy" holds its GB/s
+against that achievable rate, "frac_hbm_peak" against the 8 TB/s
+specification.  "cpu_baseline" is the CPU oracle timed on a
 bounded sample of the same step and extrapolated to the full step (rank 0,
 one thread).
 """
@@ -396,6 +399,21 @@ def _traffic(workload: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+
+
+def measure_copy_gbs(ev: "HipEvents") -> float:
+    """What this GPU sustains for a plain device copy (1 GiB, MALL-cold):
+    bytes read + bytes written over the median time of 3 blocks of 3 copies
+    -- the ceiling the bandwidth-bound casts are held against beside the 8 TB/s
+    spec figure."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = _time_ms(lambda: dst.copy_(src), 3, ev)
+    del src, dst
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
 def calibrate_copy(nbytes: int):
     """A plain device-to-device copy of known size: what FETCH_SIZE / WRITE_SIZE
     read for it scales the counters taken on the path's kernels."""
@@ -531,6 +549,7 @@ def main():
         ev.record(0, True)
         torch.cuda.synchronize()
         op_ms.append(ev.ms(0) / reps)
+    copy_gbs = measure_copy_gbs(ev)
     kernels = {}
     for (name, kind, work, _), ms in zip(step.ops, op_ms):
         ent = {"ms": round(ms, 4)}
@@ -540,7 +559,7 @@ def main():
         elif kind == "quant":
             gbs = work / (ms * 1e-3) / 1e9
             ent.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                        "algorithmic_bytes": work})
+                        "frac_copy": round(gbs / copy_gbs, 4), "algorithmic_bytes": work})
         kernels[name] = ent
 
     # dominant kernel: the GEMM with the largest share of the step
@@ -592,6 +611,9 @@ def main():
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                      "launches_timed": len(dom_launch_ms)},
         "kernels": kernels,
+        "hbm_copy": {"gbs": round(copy_gbs, 1), "bytes": COPY_BYTES,
+                     "note": "device-to-device copy on this GPU, read + write bytes / time; frac_copy of a cast is "
+                             "its algorithmic GB/s over this"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -377,10 +377,15 @@ def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
 # ---------------------------------------------------------------------------
 
 def _source_sha() -> str:
+    """Hash of the sources that define the kernels and their launch
+    configuration (the HIP files and the two internal headers; the C ABI's
+    host-side validation in api.cpp does not change what a kernel moves)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "fp8_scaled_quantization_scale_amd", "csrc"))):
-        with open(os.path.join(ROOT, "fp8_scaled_quantization_scale_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "fp8_scaled_quantization_scale_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith(".hip") or f in ("device.hpp", "launch.hpp"):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -21,6 +21,9 @@ int hip_status(hipError_t e) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// the persistent GEMM grid numbers its 256 x 256 output tiles with 32-bit ints
+bool tile_count_ok(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256) <= 0x7FFFFFFFLL; }
+
 int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int recipe,
                    int fmt, int orient, int margin, const uint8_t* q_row, int64_t ld_q_row,
                    const void* s_row, const uint8_t* q_col, int64_t ld_q_col, const void* s_col,
@@ -77,6 +80,7 @@ int check_gemm(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const 
   if (M > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL) return FP8MI_ERR_UNSUPPORTED;
   // operand panels are addressed with 32-bit buffer offsets
   if (K > 0 && (lda > (1LL << 22) || ldb > (1LL << 22))) return FP8MI_ERR_UNSUPPORTED;
+  if (!tile_count_ok(M, N)) return FP8MI_ERR_UNSUPPORTED;
   return FP8MI_OK;
 }
 
@@ -132,6 +136,7 @@ int fp8_bf16_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
   }
   if (M > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x3FFFFFFFLL) return FP8MI_ERR_UNSUPPORTED;
   if (K > 0 && (lda > (1LL << 21) || ldb > (1LL << 21))) return FP8MI_ERR_UNSUPPORTED;
+  if (!tile_count_ok(M, N)) return FP8MI_ERR_UNSUPPORTED;
   fp8mi::GemmParams p{reinterpret_cast<const uint8_t*>(a), 0, nullptr, lda, reinterpret_cast<const uint8_t*>(b), 0,
                       nullptr, ldb, FP8MI_GEMM_TENSOR, M, N, K, c, c_dtype, ldc};
   return hip_status(fp8mi::launch_gemm_bf16(p, (hipStream_t)stream));

@@ -208,8 +208,9 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  *   scales the FP32 result by s_a[i] * s_b[j] (the rows of a and b are the
  *   channels: a per-row scale of X and a per-output-channel scale of W).
  * Requirements: M, N, K >= 0; K % 16 == 0; a, b 16-byte aligned,
- * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 (else
- * FP8MI_ERR_UNSUPPORTED); ldc >= N.  K == 0 writes zeros.
+ * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 and
+ * ceil(M/256) * ceil(N/256) < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N.
+ * K == 0 writes zeros.
  * Tolerance vs a float64 reference over the dequantized operands:
  * |C - C_ref| <= 2^-10 sum_k |a b| (+ 2^-8 |C_ref| for BF16 output). */
 int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,
@@ -226,8 +227,8 @@ int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,
  *   a [M x K] BF16, lda; b [N x K] BF16, ldb (elements, K contiguous);
  *   c [M x N] (c_dtype), ldc.  C[i][j] = sum_k a[i][k] * b[j][k].
  * Requirements: M, N, K >= 0; K % 8 == 0; a, b 16-byte aligned, lda, ldb
- * multiples of 8, K <= lda, ldb <= 2097152 (else FP8MI_ERR_UNSUPPORTED);
- * ldc >= N.  K == 0 writes zeros.  Errors as for fp8_gemm_scaled.
+ * multiples of 8, K <= lda, ldb <= 2097152 and ceil(M/256) * ceil(N/256)
+ * < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N.  K == 0 writes zeros.  Errors as for fp8_gemm_scaled.
  * Tolerance vs a float64 reference: as fp8_gemm_scaled. */
 int fp8_bf16_gemm(const void* a, int64_t lda, const void* b, int64_t ldb,
                   int64_t M, int64_t N, int64_t K,

@@ -111,6 +111,7 @@ def _g(**kw):
     (dict(a=GOOD + 1), fm.ERR_ALIGN),
     (dict(ldb=264 - 4), fm.ERR_ALIGN),
     (dict(lda=(1 << 22) + 16), fm.ERR_UNSUPPORTED),
+    (dict(M=0x7FFFFFFF, N=0x7FFFFFFF, ldc=0x7FFFFFFF), fm.ERR_UNSUPPORTED),  # tile count past 2^31
 ])
 def test_gemm_validation(kw, code):
     assert _g(**kw) == code
@@ -147,6 +148,7 @@ def _b(**kw):
     (dict(a=GOOD + 8), fm.ERR_ALIGN),
     (dict(lda=260), fm.ERR_ALIGN),
     (dict(lda=(1 << 21) + 8), fm.ERR_UNSUPPORTED),
+    (dict(M=0x7FFFFFFF, N=0x7FFFFFFF, ldc=0x7FFFFFFF), fm.ERR_UNSUPPORTED),
 ])
 def test_bf16_gemm_validation(kw, code):
     assert _b(**kw) == code

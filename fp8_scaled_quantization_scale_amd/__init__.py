@@ -81,7 +81,28 @@ def _p(t) -> int | None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise Fp8Error("tensor arguments must be device tensors (the kernels read and write them on the GPU)")
     return t.data_ptr()
+
+
+def _need(ok: bool, msg: str):
+    if not ok:
+        raise Fp8Error(msg)
+
+
+def _matrix(name: str, t, dtypes) -> None:
+    """A 2-D device tensor with unit column stride and one of `dtypes`."""
+    _need(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a device tensor")
+    _need(t.dim() == 2 and t.stride(1) == 1, f"{name} must be 2-D with unit column stride")
+    _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+
+
+def _vector(name: str, t, dtype, n: int) -> None:
+    """A contiguous device tensor of `dtype` holding at least `n` elements."""
+    _need(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a device tensor")
+    _need(t.dtype == dtype, f"{name} has dtype {t.dtype}; expected {dtype}")
+    _need(t.is_contiguous() and t.numel() >= n, f"{name} must be contiguous with at least {n} elements")
 
 
 def _stream(stream) -> int | None:
@@ -179,7 +200,14 @@ def quantize(x: torch.Tensor, recipe: int, fmt: int, orient: int = ROW, margin: 
              scale: torch.Tensor | None = None, amax: torch.Tensor | None = None,
              nonfinite: torch.Tensor | None = None, stream=None) -> Quantized:
     """Quantize a 2-D BF16/FP32 device tensor (row-major, ld = its stride)."""
-    assert x.dim() == 2 and x.stride(1) == 1
+    _matrix("x", x, (torch.bfloat16, torch.float32))
+    if scale is not None:
+        _vector("scale", scale, torch.float32, 1)
+    if amax is not None:
+        _need(isinstance(amax, torch.Tensor) and amax.is_cuda and amax.dtype == torch.float32
+              and amax.is_contiguous(), "amax must be a contiguous float32 device tensor")
+    if nonfinite is not None:
+        _vector("nonfinite", nonfinite, torch.int32, 1)
     rows, cols = x.shape
     dev = x.device
     x_dtype = IN_BF16 if x.dtype == torch.bfloat16 else IN_FP32
@@ -213,16 +241,53 @@ def quantize(x: torch.Tensor, recipe: int, fmt: int, orient: int = ROW, margin: 
     return out
 
 
+_OUT_DTYPES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_FP32}
+
+
+def _scale_need(recipe: int, rows: int, K: int, is_a: bool):
+    """(elements, dtype) of the scale grid fp8_gemm_scaled reads for one
+    operand with `rows` rows (M for a, N for b) and contraction K."""
+    kb = _ceil(K, 128)
+    if recipe == GEMM_TENSOR:
+        return 1, torch.float32
+    if recipe == GEMM_CHANNEL:
+        return rows, torch.float32
+    if recipe == GEMM_MX_1x32:
+        return rows * _ceil(K, 32), torch.uint8
+    if recipe == GEMM_BLOCK_128x128_128x128 or (recipe == GEMM_BLOCK_1x128_128x128 and not is_a):
+        return _ceil(rows, 128) * kb, torch.float32
+    if recipe in (GEMM_BLOCK_1x128_128x128, GEMM_BLOCK_1x128_1x128):
+        return rows * kb, torch.float32
+    raise Fp8Error(f"unknown GEMM recipe {recipe}")
+
+
 def gemm(a: torch.Tensor, fmt_a: int, s_a: torch.Tensor, b: torch.Tensor, fmt_b: int,
          s_b: torch.Tensor, recipe: int, K: int, out_dtype=torch.bfloat16,
          M: int | None = None, N: int | None = None, c: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
-    """C[M x N] = dequant(a[:, :K]) . dequant(b[:, :K])^T (a, b uint8 codes, row-major)."""
+    """C[M x N] = dequant(a[:, :K]) . dequant(b[:, :K])^T (a, b uint8 codes, row-major).
+
+    Checks every tensor against the sizes the kernels will touch (the C entry
+    point takes plain pointers and cannot), so a wrong size is an Fp8Error
+    here rather than an out-of-bounds access on the GPU."""
+    codes = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
+    _matrix("a", a, codes)
+    _matrix("b", b, codes)
     M = a.shape[0] if M is None else M
     N = b.shape[0] if N is None else N
+    _need(M >= 0 and N >= 0 and K >= 0, "M, N, K must be non-negative")
     if c is None:
+        _need(out_dtype in _OUT_DTYPES, f"out_dtype must be one of {tuple(_OUT_DTYPES)}")
         c = torch.empty(M, N, dtype=out_dtype, device=a.device)
-    c_dtype = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_FP32
+    _matrix("c", c, tuple(_OUT_DTYPES))
+    _need(c.shape[0] >= M and c.shape[1] >= N, f"c is {tuple(c.shape)}; needs at least {M} x {N}")
+    if M > 0 and N > 0 and K > 0:
+        _need(a.shape[0] >= M and a.shape[1] >= K, f"a is {tuple(a.shape)}; needs at least {M} x {K}")
+        _need(b.shape[0] >= N and b.shape[1] >= K, f"b is {tuple(b.shape)}; needs at least {N} x {K}")
+        for name, t, (n, dt) in (("s_a", s_a, _scale_need(recipe, M, K, True)),
+                                 ("s_b", s_b, _scale_need(recipe, N, K, False))):
+            _vector(name, t, dt, n)
+    c_dtype = _OUT_DTYPES[c.dtype]
     st = fp8_gemm_scaled(a, fmt_a, s_a, a.stride(0), b, fmt_b, s_b, b.stride(0), recipe,
                          M, N, K, c, c_dtype, c.stride(0), stream)
     _check(st, "fp8_gemm_scaled")
@@ -232,12 +297,17 @@ def gemm(a: torch.Tensor, fmt_a: int, s_a: torch.Tensor, b: torch.Tensor, fmt_b:
 def bf16_gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.bfloat16,
               c: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """C[M x N] = a[M x K] . b[N x K]^T, BF16 operands (row-major, unit column stride)."""
-    assert a.dtype == b.dtype == torch.bfloat16 and a.stride(1) == 1 and b.stride(1) == 1
+    _matrix("a", a, (torch.bfloat16,))
+    _matrix("b", b, (torch.bfloat16,))
     M, K = a.shape
     N = b.shape[0]
+    _need(b.shape[1] >= K, f"b is {tuple(b.shape)}; needs at least {N} x {K}")
     if c is None:
+        _need(out_dtype in _OUT_DTYPES, f"out_dtype must be one of {tuple(_OUT_DTYPES)}")
         c = torch.empty(M, N, dtype=out_dtype, device=a.device)
-    c_dtype = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_FP32
+    _matrix("c", c, tuple(_OUT_DTYPES))
+    _need(c.shape[0] >= M and c.shape[1] >= N, f"c is {tuple(c.shape)}; needs at least {M} x {N}")
+    c_dtype = _OUT_DTYPES[c.dtype]
     _check(fp8_bf16_gemm(a, a.stride(0), b, b.stride(0), M, N, K, c, c_dtype, c.stride(0), stream),
            "fp8_bf16_gemm")
     return c

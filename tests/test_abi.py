@@ -159,11 +159,19 @@ def test_bf16_gemm_empty_is_ok_without_launch():
     assert _b(N=0, c=None) == fm.OK
 
 
-def test_binding_rejects_a_short_amax_array():
-    """Per-tensor casts take an amax array of AMAX_SLOTS floats (current
-    scaling keeps its partial maxima there); the binding refuses a shorter
-    one before any library call."""
+def test_binding_rejects_host_tensors():
+    """The kernels read and write every tensor on the GPU: the binding refuses
+    host tensors before any library call (a host pointer handed to a kernel
+    would be an out-of-bounds access, not an error)."""
     x = torch.zeros(4, 16, dtype=torch.bfloat16)
-    for recipe in (fm.TENSOR_CURRENT, fm.TENSOR_DELAYED):
-        with pytest.raises(fm.Fp8Error, match="amax"):
-            fm.quantize(x, recipe, fm.E4M3, fm.ROW, scale=torch.ones(1), amax=torch.zeros(1))
+    q = torch.zeros(4, 16, dtype=torch.uint8)
+    s1 = torch.ones(1)
+    with pytest.raises(fm.Fp8Error, match="device tensor"):
+        fm.quantize(x, fm.BLOCK_1x128, fm.E4M3, fm.ROW)
+    with pytest.raises(fm.Fp8Error, match="device tensor"):
+        fm.gemm(q, fm.E4M3, s1, q, fm.E4M3, s1, fm.GEMM_TENSOR, 16)
+    with pytest.raises(fm.Fp8Error, match="device tensor"):
+        fm.bf16_gemm(x, x)
+    with pytest.raises(fm.Fp8Error, match="device tensors"):
+        fm.fp8_gemm_scaled(q, fm.E4M3, s1, 16, q, fm.E4M3, s1, 16, fm.GEMM_TENSOR, 4, 4, 16,
+                           torch.zeros(4, 4), fm.OUT_FP32, 4, stream=0)

@@ -371,7 +371,21 @@ def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
         "sample": (f"oracle on {rows} of {M} token rows of X and G, {wrows} of {N} weight rows, and "
                    f"the {rows}x{wrows} GEMM outputs they give (float64 numpy, 1 thread); measured "
                    f"{(t3 - t0):.2f} s, extrapolated to the full step ({full:.1f} s)"),
+        "host_cpu": _cpu_model(),
+        "host_cpus_visible": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
     }
+
+
+def _cpu_model() -> str:
+    """Model name of the host CPU the baseline ran on (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---------------------------------------------------------------------------

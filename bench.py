@@ -320,10 +320,9 @@ def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
     w = workloads.make(cfg.W, rows=wrows).float().numpy()
     g = workloads.make(cfg.G, rows=rows).float().numpy()
     n_gemms = len(cfg.gemms)
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    if ctx is not None:
-        ctx.__enter__()
-    try:
+
+    def run():
+        """One pass of the oracle over the sample: (t0, t1, t2, t3)."""
         if cfg.recipe == "tensor":
             t0 = time.perf_counter()
             qx, _, six, _, _ = oracle.quantize_current("e4m3", x)
@@ -332,36 +331,55 @@ def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
             h.update(am)
             t1 = time.perf_counter()
             qw, _, siw, _, _ = oracle.quantize_current("e4m3", w)
-            qwt = np.ascontiguousarray(qw.T)
+            np.ascontiguousarray(qw.T)
             t2 = time.perf_counter()
             oracle.gemm_ref(oracle.dequant("e4m3", qx, six), oracle.dequant("e4m3", qw, siw))
             t3 = time.perf_counter()
+            return t0, t1, t2, t3
+        if cfg.recipe == "block":
+            quant = lambda v, br, bc: oracle.quantize_blocks("e4m3", v, br, bc)  # noqa: E731
+            deq = oracle.dequant
+            rb, cb, wb, wcb = (1, 128), (128, 1), (128, 128), None
         else:
-            if cfg.recipe == "block":
-                quant = lambda v, br, bc: oracle.quantize_blocks("e4m3", v, br, bc)  # noqa: E731
-                deq = oracle.dequant
-                rb, cb, wb, wcb = (1, 128), (128, 1), (128, 128), None
-            else:
-                quant = lambda v, br, bc: oracle.quantize_mx("e4m3", v, br, bc)  # noqa: E731
-                deq = oracle.dequant_mx
-                rb, cb, wb, wcb = (1, 32), (32, 1), (1, 32), (32, 1)
-            t0 = time.perf_counter()
-            qx, gx, _ = quant(x, *rb)
-            quant(x, *cb)
-            quant(g, *rb)
-            quant(g, *cb)
-            t1 = time.perf_counter()
-            qw, gw, _ = quant(w, *wb)
-            if wcb is not None:
-                quant(w, *wcb)
-            t2 = time.perf_counter()
-            oracle.gemm_ref(deq("e4m3", qx, gx, *rb), deq("e4m3", qw, gw, *wb))
-            t3 = time.perf_counter()
+            quant = lambda v, br, bc: oracle.quantize_mx("e4m3", v, br, bc)  # noqa: E731
+            deq = oracle.dequant_mx
+            rb, cb, wb, wcb = (1, 32), (32, 1), (1, 32), (32, 1)
+        t0 = time.perf_counter()
+        qx, gx, _ = quant(x, *rb)
+        quant(x, *cb)
+        quant(g, *rb)
+        quant(g, *cb)
+        t1 = time.perf_counter()
+        qw, gw, _ = quant(w, *wb)
+        if wcb is not None:
+            quant(w, *wcb)
+        t2 = time.perf_counter()
+        oracle.gemm_ref(deq("e4m3", qx, gx, *rb), deq("e4m3", qw, gw, *wb))
+        t3 = time.perf_counter()
+        return t0, t1, t2, t3
+
+    def extrapolate(t):
+        t0, t1, t2, t3 = t
+        return ((t1 - t0) * (M / rows) + (t2 - t1) * (N / wrows)
+                + (t3 - t2) * (M / rows) * (N / wrows) * n_gemms)
+
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        t0, t1, t2, t3 = run()
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    full = ((t1 - t0) * (M / rows) + (t2 - t1) * (N / wrows)
-            + (t3 - t2) * (M / rows) * (N / wrows) * n_gemms)
+    # the same sample with the float64 GEMM on every BLAS thread (the C
+    # quantizer is single-threaded either way)
+    ta = run()
+    blas_threads = 0
+    if threadpool_limits is not None:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"],
+                           default=0)
+    full = extrapolate((t0, t1, t2, t3))
     flops = n_gemms * 2.0 * M * N * K
     return {
         "value": round(flops / full / 1e12, 6),
@@ -371,6 +389,8 @@ def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
         "sample": (f"oracle on {rows} of {M} token rows of X and G, {wrows} of {N} weight rows, and "
                    f"the {rows}x{wrows} GEMM outputs they give (float64 numpy, 1 thread); measured "
                    f"{(t3 - t0):.2f} s, extrapolated to the full step ({full:.1f} s)"),
+        "all_cores": {"value": round(flops / extrapolate(ta) / 1e12, 6), "blas_threads": blas_threads,
+                      "note": "same sample, float64 GEMM on every BLAS thread; the C quantizer stays on one"},
         "host_cpu": _cpu_model(),
         "host_cpus_visible": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
     }

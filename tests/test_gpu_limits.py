@@ -1,0 +1,113 @@
+"""Parity at the largest sizes the C ABI accepts.
+
+fp8_gemm_scaled takes K and leading dimensions up to 2^22 bytes (operand
+panels are addressed with 32-bit buffer offsets: 256 rows x 2^22 = 2^30),
+and fp8_quantize up to 65535 tiles of 128 rows.  These tests run those
+extremes and compare sampled outputs with the oracle: GEMM entries against
+the float64 dot product of the dequantized rows (random operand codes with
+random signs, so the FP32 accumulation error stays far inside the
+2^-10 sum|ab| bound even at K = 2^22), quantized rows and 128-row column
+blocks against the oracle's blockwise cast of the same rows."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_quantization_scale_amd as fm
+import oracle
+import workloads
+from gpu_util import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+KMAX = 1 << 22  # the largest K / lda / ldb fp8_gemm_scaled accepts
+
+
+def _codes(rows, cols, seed):
+    """Random E4M3 codes on the device, the two NaN codes replaced by zero."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = torch.randint(0, 256, (rows, cols), dtype=torch.uint8, device="cuda", generator=g)
+    q[(q & 0x7F) == 0x7F] = 0
+    return q
+
+
+def _host_row(t, i):
+    return t[i].cpu().numpy()
+
+
+@pytest.mark.parametrize("recipe", [fm.GEMM_TENSOR, fm.GEMM_BLOCK_1x128_128x128, fm.GEMM_MX_1x32])
+def test_gemm_at_the_largest_k(recipe):
+    need_gpu()
+    M, N, K = 512, 256, KMAX
+    a, b = _codes(M, K, 71), _codes(N, K, 72)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(73)
+    kb = K // 128
+    if recipe == fm.GEMM_TENSOR:
+        s_a = torch.tensor([0.03125], device="cuda")
+        s_b = torch.tensor([0.0078125], device="cuda")
+    elif recipe == fm.GEMM_BLOCK_1x128_128x128:
+        # arbitrary positive float32 block scales
+        s_a = torch.exp2(torch.rand(M, kb, device="cuda", generator=g) * 6 - 9).float()
+        s_b = torch.exp2(torch.rand(N // 128, kb, device="cuda", generator=g) * 6 - 9).float()
+    else:
+        s_a = torch.randint(118, 126, (M, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+        s_b = torch.randint(118, 126, (N, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    c = fm.gemm(a, fm.E4M3, s_a, b, fm.E4M3, s_b, recipe, K)
+    torch.cuda.synchronize()
+    e8m0 = np.array([oracle.e8m0_value(v) for v in range(256)])
+    rng = np.random.default_rng(74)
+    pairs = [(0, 0), (M - 1, N - 1), (255, 128), (256, 127)] + \
+        [(int(i), int(j)) for i, j in zip(rng.integers(0, M, 8), rng.integers(0, N, 8))]
+    got = c.float().cpu().numpy()
+    sa_h, sb_h = s_a.cpu().numpy(), s_b.cpu().numpy()
+    for i, j in pairs:
+        va = oracle.decode("e4m3", _host_row(a, i))
+        vb = oracle.decode("e4m3", _host_row(b, j))
+        if recipe == fm.GEMM_TENSOR:
+            va, vb = va * float(sa_h[0]), vb * float(sb_h[0])
+        elif recipe == fm.GEMM_BLOCK_1x128_128x128:
+            va = va * np.repeat(sa_h[i].astype(np.float64), 128)
+            vb = vb * np.repeat(sb_h[j // 128].astype(np.float64), 128)
+        else:
+            va = va * np.repeat(e8m0[sa_h[i]], 32)
+            vb = vb * np.repeat(e8m0[sb_h[j]], 32)
+        ref, s = oracle.gemm_ref_entries(va[None, :], vb[None, :], [0], [0])
+        bad = oracle.gemm_violations(np.array([got[i, j]]), ref, s, "bf16")
+        assert not bad.any(), (recipe, i, j, got[i, j], ref[0], s[0])
+
+
+@pytest.mark.parametrize("recipe", [fm.BLOCK_1x128, fm.MX_1x32, fm.TENSOR_CURRENT])
+def test_quantize_at_the_most_row_tiles(recipe):
+    """65535 tiles of 128 rows (8388480 rows) of 16 columns, both layouts."""
+    need_gpu()
+    rows, cols = 65535 * 128, 16
+    x = workloads.make(workloads.Tensor("X", rows, cols, "outliers", 1.0, 81, 0.02, 50.0), "cuda")
+    orient = fm.ROW if recipe == fm.TENSOR_CURRENT else fm.ROW_AND_COL
+    q = fm.quantize(x, recipe, fm.E4M3, orient)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(82)
+    rsel = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 32)]))
+    xr = x[torch.as_tensor(rsel, device="cuda")].float().cpu().numpy()
+    if recipe == fm.TENSOR_CURRENT:
+        a = oracle.amax(x.float().cpu().numpy())
+        s, s_inv, _ = oracle.scale_from_amax("e4m3", a)
+        assert np.float32(q.amax[0].item()) == np.float32(a)
+        oq, _ = oracle.quantize_delayed("e4m3", xr, s)
+        assert np.array_equal(q.q_row[torch.as_tensor(rsel, device="cuda")][:, :cols].cpu().numpy(), oq)
+        return
+    br, bc = (1, 128) if recipe == fm.BLOCK_1x128 else (1, 32)
+    qfun = (lambda v, r, c_: oracle.quantize_blocks("e4m3", v, r, c_)) if recipe == fm.BLOCK_1x128 else \
+        (lambda v, r, c_: oracle.quantize_mx("e4m3", v, r, c_))
+    oq, og, _ = qfun(xr, br, bc)
+    assert np.array_equal(q.q_row[torch.as_tensor(rsel, device="cuda")][:, :cols].cpu().numpy(), oq)
+    assert np.array_equal(q.s_row[torch.as_tensor(rsel, device="cuda")].cpu().numpy(), og)
+    # column blocks along the rows: 128 (1x128) or 32 (MX) rows each
+    cb = 128 if recipe == fm.BLOCK_1x128 else 32
+    nblk = rows // cb
+    for blk in (0, nblk - 1, int(rng.integers(0, nblk))):
+        r0 = blk * cb
+        xb = x[r0:r0 + cb].float().cpu().numpy()
+        oq, og, _ = qfun(xb, cb, 1)
+        assert np.array_equal(q.q_col[:, r0:r0 + cb].cpu().numpy(), oq.T), blk
+        assert np.array_equal(q.s_col[:, blk].cpu().numpy(), og[0]), blk

@@ -6,24 +6,31 @@ One step = one pass of the whole path over one batch of synthetic inputs:
 quantize every GEMM operand with the workload's recipe (including the
 transposed layouts the backward GEMMs read), the delayed-scaling history
 update where the recipe has one, then the fprop / dgrad (/ wgrad) scaled FP8
-GEMMs.  Inputs are resident in HBM before timing starts; R rotating copies of
-every input (default 4, > 256 MB in total) keep each step's reads from being
-served by the previous step's Infinity Cache contents.
+GEMMs.  The default workload is one GPU's full Llama-3.1-405B MLP layer in
+the blockwise recipe (X 8192 x 16384, W 53248 x 16384, G 8192 x 53248;
+transpose-quantize inside the timing).  Inputs are resident in HBM before
+timing starts; R rotating copies of every input (default 4) keep each step's
+reads from being served by the previous step's Infinity Cache contents.
 
 Prints ONE JSON line.  `value` is GEMM FLOP of the step / step time (TFLOP/s),
-so quantization time counts against it.  Per-kernel figures (TFLOP/s or GB/s
-against the MI355X peaks) are under "kernels", each op timed on its own over
-back-to-back launches; "roofline" is the dominant kernel's, timed inside the
-timed steps with HIP events on the stream it runs on, in every 4th step
-(--event-every).  The events are created without the system-scope release
-fence (a fenced event writes back and invalidates the caches and stalls the
-queue for several microseconds); even so each record costs the queue about
-4.5 us, which is why not every step carries them.  "hbm_copy" is a 1 GiB
-device copy timed on the same GPU: each cast's "frac_copy" holds its GB/s
-against that achievable rate, "frac_hbm_peak" against the 8 TB/s
-specification.  "cpu_baseline" is the CPU oracle timed on a
-bounded sample of the same step and extrapolated to the full step (rank 0,
-one thread).
+so quantization time counts against it.
+  * "roofline": the dominant GEMM (largest share of the step), timed inside
+    the timed steps with HIP events on the stream it runs on, in every E-th
+    step (--event-every); "roofline_fprop" the same for the fprop GEMM, the
+    blockwise kernel the method's throughput target names.  Each carries the
+    fraction of the 5.0 PFLOP/s datasheet peak and of the rate the matrix
+    cores sustain on this GPU under full FP8 load ("mfma_ceiling", measured
+    by libfp8mi_probe.so together with the shader clock under that load).
+  * "kernels": each op alone over back-to-back launches; casts report GB/s
+    against the 8 TB/s datasheet figure and against "hbm_ceiling", in-tree
+    streaming kernels at the cast's own read:write byte mix.
+  * "event_pair_empty_us": what one pair of (fence-free) event records costs
+    the queue, measured on an empty stretch of it.
+  * "cpu_baseline": the CPU oracle timed on a bounded sample of the step and
+    extrapolated to the full step (rank 0), on one thread and on every core.
+`--workload tiny_block` (a parity-size case) prints a latency line instead:
+microseconds per step (quantize A 1x128, quantize B 128x128, fprop GEMM),
+launched eagerly and as a replayed HIP graph.
 """
 from __future__ import annotations
 
@@ -42,11 +49,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import fp8_scaled_quantization_scale_amd as fm  # noqa: E402
+from fp8_scaled_quantization_scale_amd import probe  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 / MXFP8 matrix peak, TFLOP/s
-DEFAULT_WORKLOAD = "llama3_8b_attn_tensor"
+PEAK_CLOCK_GHZ = 2.4          # the clock the datasheet peak assumes
+DEFAULT_WORKLOAD = "llama31_405b_mlp_block"
 
 
 # ---------------------------------------------------------------------------
@@ -121,12 +130,12 @@ class Step:
 
         def fprop(r):
             _ok(fm.fp8_gemm_scaled(self.qx, fm.E4M3, self.six, K, self.qw, fm.E4M3, self.siw, K,
-                                   fm.GEMM_TENSOR, M, N, K, self.y, fm.OUT_BF16, N))
+                                   fm.GEMM_TENSOR, fm.LAYOUT_TN, M, N, K, self.y, fm.OUT_BF16, N))
 
         def dgrad(r):
             # dX[M x K] = dY[M x N] . W[N x K]: A = dY codes, B = W^T codes [K x N]
             _ok(fm.fp8_gemm_scaled(self.qg, fm.E5M2, st.scale_inv, N, self.qwt, fm.E4M3, self.siw, N,
-                                   fm.GEMM_TENSOR, M, K, N, self.dx, fm.OUT_BF16, K))
+                                   fm.GEMM_TENSOR, fm.LAYOUT_TN, M, K, N, self.dx, fm.OUT_BF16, K))
 
         # the history update closes the step: dgrad must dequantize G's codes
         # with the scale_inv they were cast with, and the update replaces it
@@ -170,16 +179,16 @@ class Step:
 
         def fprop(r):
             _ok(fm.fp8_gemm_scaled(self.qx, fm.E4M3, self.sx, K, self.qw, fm.E4M3, self.sw, K,
-                                   fm.GEMM_BLOCK_1x128_128x128, M, N, K, self.y, fm.OUT_BF16, N))
+                                   fm.GEMM_BLOCK_1x128_128x128, fm.LAYOUT_TN, M, N, K, self.y, fm.OUT_BF16, N))
 
         def dgrad(r):
             _ok(fm.fp8_gemm_scaled(self.qg, fm.E4M3, self.sg, N, self.qwt, fm.E4M3, self.swt, N,
-                                   fm.GEMM_BLOCK_1x128_128x128, M, K, N, self.dx, fm.OUT_BF16, K))
+                                   fm.GEMM_BLOCK_1x128_128x128, fm.LAYOUT_TN, M, K, N, self.dx, fm.OUT_BF16, K))
 
         def wgrad(r):
             # dW[N x K] = dY^T[N x M] . X[M x K]: both operands blocked along M
             _ok(fm.fp8_gemm_scaled(self.qgt, fm.E4M3, self.sgt, M, self.qxt, fm.E4M3, self.sxt, M,
-                                   fm.GEMM_BLOCK_1x128_1x128, N, K, M, self.dw, fm.OUT_BF16, K))
+                                   fm.GEMM_BLOCK_1x128_1x128, fm.LAYOUT_TN, N, K, M, self.dw, fm.OUT_BF16, K))
 
         sc = 4 / 128
         self.ops = [
@@ -214,15 +223,15 @@ class Step:
 
         def fprop(r):
             _ok(fm.fp8_gemm_scaled(self.qx, fm.E4M3, self.sx, K, self.qw, fm.E4M3, self.sw, K,
-                                   fm.GEMM_MX_1x32, M, N, K, self.y, fm.OUT_BF16, N))
+                                   fm.GEMM_MX_1x32, fm.LAYOUT_TN, M, N, K, self.y, fm.OUT_BF16, N))
 
         def dgrad(r):
             _ok(fm.fp8_gemm_scaled(self.qg, fm.E4M3, self.sg, N, self.qwt, fm.E4M3, self.swt, N,
-                                   fm.GEMM_MX_1x32, M, K, N, self.dx, fm.OUT_BF16, K))
+                                   fm.GEMM_MX_1x32, fm.LAYOUT_TN, M, K, N, self.dx, fm.OUT_BF16, K))
 
         def wgrad(r):
             _ok(fm.fp8_gemm_scaled(self.qgt, fm.E4M3, self.sgt, M, self.qxt, fm.E4M3, self.sxt, M,
-                                   fm.GEMM_MX_1x32, N, K, M, self.dw, fm.OUT_BF16, K))
+                                   fm.GEMM_MX_1x32, fm.LAYOUT_TN, N, K, M, self.dw, fm.OUT_BF16, K))
 
         b = 2 + 1 + 1 + 2 / 32
         self.ops = [
@@ -303,12 +312,21 @@ def _ok(status: int):
 # CPU oracle baseline on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
-    """Time the oracle on a bounded sample of the step -- `rows` token rows of
-    X and G, `wrows` rows of W, and the GEMM outputs of those rows -- and
-    extrapolate to the full step: token-row costs x M/rows, weight-row costs
-    x N/wrows, GEMM cost x (M/rows)(N/wrows) per GEMM (dgrad and wgrad do the
-    same contraction work as fprop)."""
+def _threads() -> int:
+    return len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+
+def cpu_baseline(cfg: workloads.Config, rows: int = 512, out_rows: int = 512):
+    """Time the oracle on a bounded sample of the step and extrapolate to the
+    full step.  Quantize: `rows` whole rows of X, G and W (their codes and
+    scales in every layout the step writes), cost scaled by M / rows (X, G)
+    and N / rows (W).  GEMMs: an out_rows x out_rows block of each GEMM's
+    output from oracle-quantized operand rows of that GEMM's contraction
+    length (dequantize, float64 product), cost scaled by the output count.
+    Timed on one thread, then with the quantize rows split over every core
+    and the float64 products on every BLAS thread."""
+    from concurrent.futures import ThreadPoolExecutor
+
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
@@ -316,83 +334,118 @@ def cpu_baseline(cfg: workloads.Config, rows: int = 1024, wrows: int = 1024):
     import oracle
 
     M, N, K = cfg.M, cfg.N, cfg.K
-    x = workloads.make(cfg.X, rows=rows).float().numpy()
-    w = workloads.make(cfg.W, rows=wrows).float().numpy()
-    g = workloads.make(cfg.G, rows=rows).float().numpy()
-    n_gemms = len(cfg.gemms)
+    draw = lambda t, r, cols=None: workloads.make(  # noqa: E731
+        t if cols is None else workloads.Tensor(t.name, r, cols, t.kind, t.sigma, t.seed, t.frac, t.factor),
+        rows=r).float().numpy()
+    x, g, w = draw(cfg.X, rows), draw(cfg.G, rows), draw(cfg.W, rows)
+    rec = cfg.recipe
 
-    def run():
-        """One pass of the oracle over the sample: (t0, t1, t2, t3)."""
-        if cfg.recipe == "tensor":
-            t0 = time.perf_counter()
-            qx, _, six, _, _ = oracle.quantize_current("e4m3", x)
-            h = oracle.History("e5m2", 200)
-            qg, am = oracle.quantize_delayed("e5m2", g, h.scale)
-            h.update(am)
-            t1 = time.perf_counter()
-            qw, _, siw, _, _ = oracle.quantize_current("e4m3", w)
-            np.ascontiguousarray(qw.T)
-            t2 = time.perf_counter()
-            oracle.gemm_ref(oracle.dequant("e4m3", qx, six), oracle.dequant("e4m3", qw, siw))
-            t3 = time.perf_counter()
-            return t0, t1, t2, t3
-        if cfg.recipe == "block":
-            quant = lambda v, br, bc: oracle.quantize_blocks("e4m3", v, br, bc)  # noqa: E731
-            deq = oracle.dequant
-            rb, cb, wb, wcb = (1, 128), (128, 1), (128, 128), None
+    def q_rows(v, br, bc):
+        if rec == "mx":
+            return oracle.quantize_mx("e4m3", v, br, bc)
+        return oracle.quantize_blocks("e4m3", v, br, bc)
+
+    def deq(q, gr, br, bc):
+        if rec == "mx":
+            return oracle.dequant_mx("e4m3", q, gr, br, bc)
+        return oracle.dequant("e4m3", q, gr, br, bc)
+
+    # layouts written per tensor: (tensor rows, its full row count, how)
+    if rec == "tensor":
+        jobs = [(x, M, "current"), (w, N, "current_t"), (g, M, "delayed")]
+    elif rec == "block":
+        jobs = [(x, M, (1, 128)), (x, M, (128, 1)), (w, N, (128, 128)), (w, N, "t128"), (g, M, (1, 128)),
+                (g, M, (128, 1))]
+    else:
+        jobs = [(v, full, bl) for v, full in ((x, M), (w, N), (g, M)) for bl in ((1, 32), (32, 1))]
+
+    def quant_job(v, how):
+        if how == "current":
+            oracle.quantize_current("e4m3", v)
+        elif how == "current_t":
+            q = oracle.quantize_current("e4m3", v)[0]
+            np.ascontiguousarray(q.T)
+        elif how == "delayed":
+            oracle.quantize_delayed("e5m2", v, 1.0)
+        elif how == "t128":
+            q_rows(np.ascontiguousarray(v.T), 128, 128)
         else:
-            quant = lambda v, br, bc: oracle.quantize_mx("e4m3", v, br, bc)  # noqa: E731
-            deq = oracle.dequant_mx
-            rb, cb, wb, wcb = (1, 32), (32, 1), (1, 32), (32, 1)
-        t0 = time.perf_counter()
-        qx, gx, _ = quant(x, *rb)
-        quant(x, *cb)
-        quant(g, *rb)
-        quant(g, *cb)
-        t1 = time.perf_counter()
-        qw, gw, _ = quant(w, *wb)
-        if wcb is not None:
-            quant(w, *wcb)
-        t2 = time.perf_counter()
-        oracle.gemm_ref(deq("e4m3", qx, gx, *rb), deq("e4m3", qw, gw, *wb))
-        t3 = time.perf_counter()
-        return t0, t1, t2, t3
+            q_rows(v, *how)
 
-    def extrapolate(t):
-        t0, t1, t2, t3 = t
-        return ((t1 - t0) * (M / rows) + (t2 - t1) * (N / wrows)
-                + (t3 - t2) * (M / rows) * (N / wrows) * n_gemms)
+    def quant_parallel(ex, v, how, n):
+        """Column chunks of whole blocks on n threads (per-tensor current
+        scaling needs the whole tensor's amax first: one thread)."""
+        if how in ("current", "current_t"):
+            quant_job(v, how)
+            return
+        cols = v.shape[1]
+        step = -(-cols // n // 128) * 128
+        parts = [np.ascontiguousarray(v[:, c0:c0 + step]) for c0 in range(0, cols, step)]
+        list(ex.map(lambda p: quant_job(p, how), parts))
+
+    def gemm_operands(kc, ta, tb):
+        """oracle-quantized, dequantized operand rows with contraction kc"""
+        a = draw(ta, out_rows, kc)
+        b = draw(tb, out_rows, kc)
+        if rec == "tensor":
+            qa, _, sa, _, _ = oracle.quantize_current("e4m3", a)
+            qb, _, sb, _, _ = oracle.quantize_current("e4m3", b)
+            return oracle.dequant("e4m3", qa, sa), oracle.dequant("e4m3", qb, sb)
+        bl = (1, 32) if rec == "mx" else (1, 128)
+        qa, ga, _ = q_rows(a, *bl)
+        qb, gb, _ = q_rows(b, *bl)
+        return deq(qa, ga, *bl), deq(qb, gb, *bl)
+
+    shapes = {"fprop": (M, N, K, cfg.X, cfg.W), "dgrad": (M, K, N, cfg.G, cfg.W),
+              "wgrad": (N, K, M, cfg.G, cfg.X)}
+
+    def run(parallel: bool):
+        """(quantize seconds, GEMM seconds, wall seconds of the sample), the
+        first two extrapolated to the full step"""
+        t0 = time.perf_counter()
+        tq = 0.0
+        with ThreadPoolExecutor(_threads()) as ex:
+            for v, full, how in jobs:
+                t1 = time.perf_counter()
+                if parallel:
+                    quant_parallel(ex, v, how, _threads())
+                else:
+                    quant_job(v, how)
+                tq += (time.perf_counter() - t1) * full / v.shape[0]
+        tg = 0.0
+        for name in cfg.gemms:
+            m, n, kc, ta, tb = shapes[name]
+            da, db = gemm_operands(kc, ta, tb)
+            t1 = time.perf_counter()
+            oracle.gemm_ref(da, db)
+            tg += (time.perf_counter() - t1) * (m * n) / (out_rows * out_rows)
+        return tq, tg, time.perf_counter() - t0
 
     ctx = threadpool_limits(1) if threadpool_limits else None
     if ctx is not None:
         ctx.__enter__()
     try:
-        t0, t1, t2, t3 = run()
+        q1, g1, wall1 = run(False)
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    # the same sample with the float64 GEMM on every BLAS thread (the C
-    # quantizer is single-threaded either way)
-    ta = run()
-    blas_threads = 0
-    if threadpool_limits is not None:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"],
-                           default=0)
-    full = extrapolate((t0, t1, t2, t3))
-    flops = n_gemms * 2.0 * M * N * K
+    qa, ga, walla = run(True)
+    flops = len(cfg.gemms) * 2.0 * M * N * K
+    full1, fulla = q1 + g1, qa + ga
     return {
-        "value": round(flops / full / 1e12, 6),
+        "value": round(flops / full1 / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"oracle on {rows} of {M} token rows of X and G, {wrows} of {N} weight rows, and "
-                   f"the {rows}x{wrows} GEMM outputs they give (float64 numpy, 1 thread); measured "
-                   f"{(t3 - t0):.2f} s, extrapolated to the full step ({full:.1f} s)"),
-        "all_cores": {"value": round(flops / extrapolate(ta) / 1e12, 6), "blas_threads": blas_threads,
-                      "note": "same sample, float64 GEMM on every BLAS thread; the C quantizer stays on one"},
+        "sample": (f"oracle quantize of {rows} whole rows of X, G and W in every layout of the step and an "
+                   f"{out_rows}x{out_rows} block of each GEMM's output (float64), on one thread; measured "
+                   f"{wall1:.1f} s, extrapolated to the full step ({full1:.1f} s: quantize {q1:.1f} s scaled "
+                   f"by rows, GEMMs {g1:.1f} s scaled by output count)"),
+        "all_cores": {"value": round(flops / fulla / 1e12, 6), "cores": _threads(),
+                      "note": f"same sample, quantize split by column blocks over {_threads()} threads, float64 products on "
+                              f"every BLAS thread; measured {walla:.1f} s, extrapolated {fulla:.1f} s"},
         "host_cpu": _cpu_model(),
-        "host_cpus_visible": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
+        "host_cpus_visible": _threads(),
     }
 
 
@@ -438,30 +491,61 @@ def _traffic(workload: str, kernel: str):
     return ent.get("bytes_per_launch")
 
 
-COPY_BYTES = 1 << 30
+CEIL_BYTES = 1 << 30  # source bytes of each ceiling stream (4x the Infinity Cache)
+MIX_OF = {"ROW": probe.HALF, "ROW_AND_COL": probe.SPLIT, "COPY": probe.COPY, "READ": probe.READ}
 
 
-def measure_copy_gbs(ev: "HipEvents") -> float:
-    """What this GPU sustains for a plain device copy (1 GiB, MALL-cold):
-    bytes read + bytes written over the median time of 3 blocks of 3 copies
-    -- the ceiling the bandwidth-bound casts are held against beside the 8 TB/s
-    spec figure."""
-    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    ms = _time_ms(lambda: dst.copy_(src), 3, ev)
-    del src, dst
-    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+def hbm_ceilings(ev: "HipEvents") -> dict:
+    """GB/s this GPU sustains for plain in-tree streams (libfp8mi_probe.so)
+    at each read:write byte mix: READ, COPY (1:1), ROW (2 bytes in, 1 out: a
+    cast writing one code layout) and ROW_AND_COL (2 in, 1 + 1 out: both
+    layouts).  1 GiB of source, median of 3 blocks of 3 passes; bytes read +
+    written over the time."""
+    src = torch.empty(CEIL_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    d0 = torch.empty(CEIL_BYTES, dtype=torch.uint8, device="cuda")
+    d1 = torch.empty(CEIL_BYTES // 2, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, mix in MIX_OF.items():
+        ms = _time_ms(lambda: probe.stream(src, d0, d1 if mix == probe.SPLIT else None, mix), 3, ev)
+        moved = CEIL_BYTES + {probe.READ: 0, probe.COPY: CEIL_BYTES, probe.HALF: CEIL_BYTES // 2,
+                              probe.SPLIT: CEIL_BYTES}[mix]
+        out[name] = round(moved / (ms * 1e-3) / 1e9, 1)
+    del src, d0, d1
+    torch.cuda.empty_cache()
+    return out
+
+
+def mfma_ceiling(ev: "HipEvents") -> dict:
+    """FP8 matrix-core rate this GPU sustains under full load (registers only,
+    two waves per SIMD, one workgroup per compute unit), and the shader clock
+    during it from the core and wall cycle counters of every workgroup."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 60000
+    clocks = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ms = _time_ms(lambda: probe.mfma(iters, cus, clocks, sink), 1, ev)
+    flops = cus * probe.MFMA_WAVES * iters * probe.MFMA_FLOPS_PER_ROUND
+    c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
+    wall_khz = probe.wall_clock_khz()
+    ghz = float(np.median((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]))) * wall_khz / 1e6
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3), "cus": cus,
+            "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "peak_at_clock_tflops": round(PEAK_FP8_TFLOPS * ghz / PEAK_CLOCK_GHZ, 1),
+            "note": "back-to-back 16x16x128 FP8 MFMAs from registers on every SIMD; clock = core cycles / "
+                    "wall cycles x the wall counter's rate, median over workgroups"}
 
 
 def calibrate_copy(nbytes: int):
-    """A plain device-to-device copy of known size: what FETCH_SIZE / WRITE_SIZE
-    read for it scales the counters taken on the path's kernels."""
+    """A plain in-tree device copy of known size (fp8probe_stream COPY): what
+    FETCH_SIZE / WRITE_SIZE read for it scales the counters taken on the
+    path's kernels."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        probe.stream(src, dst, None, probe.COPY)
     torch.cuda.synchronize()
-    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3, "kernel": "fp8probe_stream COPY"}))
 
 
 # ---------------------------------------------------------------------------
@@ -528,6 +612,70 @@ def speedup_sweep(M: int, N: int, ks, reps: int):
         torch.cuda.empty_cache()
 
 
+def latency_line(cfg: workloads.Config, args, ev: "HipEvents") -> dict:
+    """Microseconds per step of the tiny blockwise case: quantize A (1x128),
+    quantize B (128x128), fprop GEMM -- launched eagerly, and as one HIP
+    graph replayed (the captured launches are the same three)."""
+    x, w = workloads.make(cfg.X, "cuda"), workloads.make(cfg.W, "cuda")
+    M, N, K = cfg.M, cfg.N, cfg.K
+    c = lambda a, b: (a + b - 1) // b  # noqa: E731
+    qx = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    sx = torch.empty(M, c(K, 128), dtype=torch.float32, device="cuda")
+    qw = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(c(N, 128), c(K, 128), dtype=torch.float32, device="cuda")
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ops = [
+        ("quant_a_1x128", lambda: _ok(fm.fp8_quantize(x, fm.IN_BF16, M, K, K, fm.BLOCK_1x128, fm.E4M3, fm.ROW, 0,
+                                                      qx, K, sx, None, 0, None, None, None, None, None))),
+        ("quant_b_128x128", lambda: _ok(fm.fp8_quantize(w, fm.IN_BF16, N, K, K, fm.BLOCK_128x128, fm.E4M3, fm.ROW,
+                                                        0, qw, K, sw, None, 0, None, None, None, None, None))),
+        ("gemm_fprop", lambda: _ok(fm.fp8_gemm_scaled(qx, fm.E4M3, sx, K, qw, fm.E4M3, sw, K,
+                                                      fm.GEMM_BLOCK_1x128_128x128, fm.LAYOUT_TN, M, N, K, y,
+                                                      fm.OUT_BF16, N))),
+    ]
+
+    def step():
+        for _, f in ops:
+            f()
+
+    reps = 200
+    for _ in range(args.warmup):
+        step()
+    eager = _time_ms(step, reps, ev) * 1e3
+    per_op = {name: round(_time_ms(f, reps, ev) * 1e3, 2) for name, f in ops}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()  # warm the capture stream
+        with torch.cuda.graph(graph, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    replay = _time_ms(graph.replay, reps, ev) * 1e3
+    return {
+        "metric": "FP8 blockwise step latency (quantize A 1x128, quantize B 128x128, fprop GEMM)",
+        "value": round(replay, 2), "unit": "us", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": cfg.name, "recipe": cfg.recipe, "M": M, "N": N, "K": K, "inputs": "bf16",
+                   "outputs": "bf16"},
+        "eager_us": round(eager, 2), "graph_replay_us": round(replay, 2), "kernels_us": per_op,
+        "note": "latency-bound case: value is one replay of a HIP graph holding the three launches; eager_us the "
+                "same three launches issued from Python; median of 3 blocks of 200 back-to-back steps",
+    }
+
+
+def _roofline(name: str, flops: int, launch_ms, ceiling: dict, workload: str) -> dict:
+    ms = float(np.mean(launch_ms))
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "frac_of_mfma_ceiling": round(achieved / ceiling["tflops"], 4),
+            "frac_at_probe_clock": round(achieved / ceiling["peak_at_clock_tflops"], 4),
+            "traffic": _traffic(workload, name), "launches_timed": len(launch_ms),
+            "launch_ms_mean": round(ms, 4), "flops_per_launch": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,38 +683,36 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.CONFIGS))
     ap.add_argument("--rotate", type=int, default=4)
-    ap.add_argument("--event-every", type=int, default=4, metavar="E",
-                    help="bracket the dominant kernel with timing events in every E-th timed step")
+    ap.add_argument("--event-every", type=int, default=2, metavar="E",
+                    help="bracket the dominant and fprop GEMMs with timing events in every E-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the HBM and matrix-core ceiling probes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES (reference for the HBM byte counters)")
+                    help="only run a plain in-tree device copy of BYTES (reference for the HBM byte counters)")
     ap.add_argument("--speedup-sweep", action="store_true",
                     help="only print the FP8-vs-BF16 GEMM speedup over K (one JSON line per K)")
     ap.add_argument("--sweep-mn", type=int, default=8192, help="M = N of the speedup sweep")
     args = ap.parse_args()
-    if args.speedup_sweep:
-        if not torch.cuda.is_available():
-            print("bench.py needs a GPU", file=sys.stderr)
-            sys.exit(2)
-        speedup_sweep(args.sweep_mn, args.sweep_mn, SWEEP_K, 10)
-        return
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the quantize + GEMM path runs on one GPU's share)",
+              "(the quantize + GEMM path runs on one GPU's share; the sharded design is described, not run)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     fm.load()
+    if args.speedup_sweep:
+        speedup_sweep(args.sweep_mn, args.sweep_mn, SWEEP_K, 10)
+        return
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     cfg = workloads.CONFIGS[args.workload]
+    ev = HipEvents(1)
     if cfg.G is None:
-        print(f"workload {args.workload} is a parity case, not a bench line", file=sys.stderr)
-        sys.exit(2)
+        print(json.dumps(latency_line(cfg, args, ev)))
+        return
 
     step = Step(cfg, args.rotate)
     torch.cuda.synchronize()
@@ -577,7 +723,6 @@ def main():
     # per-op breakdown: each op alone, `reps` back-to-back launches over the
     # rotating input copies between one pair of events
     reps = 10
-    ev = HipEvents(1)
     op_ms = []
     for _, _, _, fn in step.ops:
         fn(0)
@@ -588,7 +733,48 @@ def main():
         ev.record(0, True)
         torch.cuda.synchronize()
         op_ms.append(ev.ms(0) / reps)
-    copy_gbs = measure_copy_gbs(ev)
+
+    # dominant kernel: the GEMM with the largest share of the step; fprop beside it
+    gemm_i = [i for i, op in enumerate(step.ops) if op[1] == "gemm"]
+    dom_i = max(gemm_i, key=lambda i: op_ms[i])
+    fprop_i = next(i for i in gemm_i if step.ops[i][0] == "gemm_fprop")
+    bracket = sorted({dom_i, fprop_i})
+
+    # the timed region: K whole steps; the bracketed GEMMs carry (fence-free)
+    # events in every E-th step
+    for i in range(2):
+        step.run(args.warmup + i)
+    sampled = [i for i in range(args.steps) if i % args.event_every == 0]
+    tev = {i: HipEvents(len(sampled)) for i in bracket}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i % args.event_every == 0:
+            j = i // args.event_every
+            for k, (_, _, _, fn) in enumerate(step.ops):
+                if k in tev:
+                    tev[k].record(j, False)
+                fn((args.warmup + i) % step.rotate)
+                if k in tev:
+                    tev[k].record(j, True)
+        else:
+            step.run(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = {k: [tev[k].ms(j) for j in range(len(sampled))] for k in bracket}
+
+    # what an empty event pair costs the queue (the bracket's own overhead)
+    empty = []
+    for _ in range(5):
+        ev.record(0, False)
+        ev.record(0, True)
+        torch.cuda.synchronize()
+        empty.append(ev.ms(0) * 1e3)
+
+    ceil_hbm = hbm_ceilings(ev) if not args.no_probes else None
+    ceil_mfma = mfma_ceiling(ev) if not args.no_probes else {"tflops": float("nan"), "peak_at_clock_tflops": float("nan")}
+
     kernels = {}
     for (name, kind, work, _), ms in zip(step.ops, op_ms):
         ent = {"ms": round(ms, 4)}
@@ -598,37 +784,14 @@ def main():
         elif kind == "quant":
             gbs = work / (ms * 1e-3) / 1e9
             ent.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                        "frac_copy": round(gbs / copy_gbs, 4), "algorithmic_bytes": work})
+                        "algorithmic_bytes": work})
+            mix = "ROW_AND_COL" if "row_col" in name else "ROW"
+            if ceil_hbm:
+                ent.update({"ceiling_mix": mix, "frac_hbm_ceiling": round(gbs / ceil_hbm[mix], 4)})
         kernels[name] = ent
 
-    # dominant kernel: the GEMM with the largest share of the step
-    dom_i = max((i for i, op in enumerate(step.ops) if op[1] == "gemm"), key=lambda i: op_ms[i])
-    dom = step.ops[dom_i]
-
-    # the timed region: K whole steps; the dominant kernel is bracketed by
-    # (fence-free) events in every EVERY-th step.  Each event record still
-    # costs the queue about 4.5 us (visible as gaps in a kernel trace), so
-    # bracketing every step would charge ~9 us of instrumentation to each.
-    for i in range(2):
-        step.run(args.warmup + i)
-    sampled = [i for i in range(args.steps) if i % args.event_every == 0]
-    tev = HipEvents(len(sampled))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i % args.event_every == 0:
-            step.run(args.warmup + i, dom_i, tev, i // args.event_every)
-        else:
-            step.run(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    dom_launch_ms = [tev.ms(j) for j in range(len(sampled))]
-
-    dom_ms = float(np.mean(dom_launch_ms))
-    achieved = dom[2] / (dom_ms * 1e-3) / 1e12
-    traffic = _traffic(args.workload, dom[0])
     value = step.gemm_flops() / (ms_step * 1e-3) / 1e12
+    dom, fp = step.ops[dom_i], step.ops[fprop_i]
     out = {
         "metric": "FP8 scaled GEMM TFLOPS (fprop/dgrad/wgrad) + quantize GB/s, % of MI355X peak",
         "value": round(value, 2),
@@ -645,14 +808,14 @@ def main():
         "config": {"workload": args.workload, "recipe": cfg.recipe, "M": cfg.M, "N": cfg.N, "K": cfg.K,
                    "gemms": list(cfg.gemms), "inputs": "bf16", "outputs": "bf16",
                    "rotating_input_copies": args.rotate},
-        "roofline": {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 1),
-                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                     "launches_timed": len(dom_launch_ms)},
+        "roofline": _roofline(dom[0], dom[2], launch_ms[dom_i], ceil_mfma, args.workload),
+        "roofline_fprop": _roofline(fp[0], fp[2], launch_ms[fprop_i], ceil_mfma, args.workload),
+        "event_pair_empty_us": round(float(np.median(empty)), 2),
         "kernels": kernels,
-        "hbm_copy": {"gbs": round(copy_gbs, 1), "bytes": COPY_BYTES,
-                     "note": "device-to-device copy on this GPU, read + write bytes / time; frac_copy of a cast is "
-                             "its algorithmic GB/s over this"},
+        "mfma_ceiling": ceil_mfma if not args.no_probes else None,
+        "hbm_ceiling": ({"gbs": ceil_hbm, "source_bytes": CEIL_BYTES,
+                         "note": "in-tree streams (libfp8mi_probe.so): bytes read + written / time; ROW = 2 bytes "
+                                 "in, 1 out; ROW_AND_COL = 2 in, 1 + 1 out"} if ceil_hbm else None),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

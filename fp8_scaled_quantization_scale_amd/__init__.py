@@ -33,6 +33,7 @@ CHANNEL, MX_1x32_OCP = 5, 6
 ROW, COL, ROW_AND_COL = 1, 2, 3
 GEMM_TENSOR, GEMM_BLOCK_1x128_128x128, GEMM_BLOCK_1x128_1x128, GEMM_MX_1x32 = 0, 1, 2, 3
 GEMM_BLOCK_128x128_128x128, GEMM_CHANNEL = 4, 5
+LAYOUT_TN = 0
 AMAX_SLOTS = 1024  # floats in the amax array of a per-tensor cast
 
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
@@ -64,7 +65,7 @@ def load(path: str = LIB_PATH):
     lib.fp8_amax_history_update.restype = i32
     lib.fp8_amax_history_update.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp, vp, vp]
     lib.fp8_gemm_scaled.restype = i32
-    lib.fp8_gemm_scaled.argtypes = [vp, i32, vp, i64, vp, i32, vp, i64, i32, i64, i64, i64,
+    lib.fp8_gemm_scaled.argtypes = [vp, i32, vp, i64, vp, i32, vp, i64, i32, i32, i64, i64, i64,
                                     vp, i32, i64, vp]
     lib.fp8_bf16_gemm.restype = i32
     lib.fp8_bf16_gemm.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i32, i64, vp]
@@ -145,9 +146,9 @@ def fp8_amax_history_update(history, head, length, amax, fmt, margin, scale, sca
                                           _p(scale), _p(scale_inv), _p(nonfinite), _stream(stream))
 
 
-def fp8_gemm_scaled(a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, M, N, K, c, c_dtype, ldc,
+def fp8_gemm_scaled(a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, layout, M, N, K, c, c_dtype, ldc,
                     stream=None) -> int:
-    return load().fp8_gemm_scaled(_p(a), fmt_a, _p(s_a), lda, _p(b), fmt_b, _p(s_b), ldb, recipe,
+    return load().fp8_gemm_scaled(_p(a), fmt_a, _p(s_a), lda, _p(b), fmt_b, _p(s_b), ldb, recipe, layout,
                                   M, N, K, _p(c), c_dtype, ldc, _stream(stream))
 
 
@@ -288,7 +289,7 @@ def gemm(a: torch.Tensor, fmt_a: int, s_a: torch.Tensor, b: torch.Tensor, fmt_b:
                                  ("s_b", s_b, _scale_need(recipe, N, K, False))):
             _vector(name, t, dt, n)
     c_dtype = _OUT_DTYPES[c.dtype]
-    st = fp8_gemm_scaled(a, fmt_a, s_a, a.stride(0), b, fmt_b, s_b, b.stride(0), recipe,
+    st = fp8_gemm_scaled(a, fmt_a, s_a, a.stride(0), b, fmt_b, s_b, b.stride(0), recipe, LAYOUT_TN,
                          M, N, K, c, c_dtype, c.stride(0), stream)
     _check(st, "fp8_gemm_scaled")
     return c

@@ -1,10 +1,11 @@
-"""Build libfp8mi.so (gfx950 HIP kernels + the C ABI) in-tree with hipcc.
+"""Build libfp8mi.so (gfx950 HIP kernels + the C ABI) and libfp8mi_probe.so
+(measurement kernels for bench.py) in-tree with hipcc.
 
     python -m fp8_scaled_quantization_scale_amd.build
 
 Every HIP translation unit is compiled with packed FP32 ops disabled
 (`-Xclang -target-feature -Xclang -packed-fp32-ops`) and FP32 divide kept
-correctly rounded (hipcc's default), then linked into one shared library
+correctly rounded (hipcc's default), then linked into the shared libraries
 next to this file.
 """
 from __future__ import annotations
@@ -23,6 +24,8 @@ LIB = os.path.join(HERE, "libfp8mi.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "quantize.hip", "history.hip", "gemm.hip"]
+PROBE_LIB = os.path.join(HERE, "libfp8mi_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -50,18 +53,24 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

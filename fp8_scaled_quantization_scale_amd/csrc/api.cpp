@@ -52,8 +52,6 @@ int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
   if (!aligned16(x) || (ld_x * esize) % 16) return FP8MI_ERR_ALIGN;
   if (row && (!aligned16(q_row) || ld_q_row % 16)) return FP8MI_ERR_ALIGN;
   if (col && (!aligned16(q_col) || ld_q_col % 16)) return FP8MI_ERR_ALIGN;
-  // grid limits of the tile launch (128 x 128 tiles, 2-D grid)
-  if ((rows + 127) / 128 > 65535 || (cols + 127) / 128 > 0x7FFFFFFF) return FP8MI_ERR_UNSUPPORTED;
   // channel scaling launches one workgroup per tile on a 1-D grid
   if (recipe == FP8MI_CHANNEL && ((rows + 127) / 128) * ((cols + 127) / 128) > 0x7FFFFFFF)
     return FP8MI_ERR_UNSUPPORTED;
@@ -61,8 +59,9 @@ int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
 }
 
 int check_gemm(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const uint8_t* b, int fmt_b,
-               const void* s_b, int64_t ldb, int recipe, int64_t M, int64_t N, int64_t K, const void* c,
-               int c_dtype, int64_t ldc) {
+               const void* s_b, int64_t ldb, int recipe, int layout, int64_t M, int64_t N, int64_t K,
+               const void* c, int c_dtype, int64_t ldc) {
+  if (layout != FP8MI_LAYOUT_TN) return FP8MI_ERR_UNSUPPORTED;
   if (fmt_a != FP8MI_E4M3 && fmt_a != FP8MI_E5M2) return FP8MI_ERR_ENUM;
   if (fmt_b != FP8MI_E4M3 && fmt_b != FP8MI_E5M2) return FP8MI_ERR_ENUM;
   if (recipe < FP8MI_GEMM_TENSOR || recipe > FP8MI_GEMM_CHANNEL) return FP8MI_ERR_ENUM;
@@ -112,9 +111,9 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
 }
 
 int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const uint8_t* b, int fmt_b,
-                    const void* s_b, int64_t ldb, int recipe, int64_t M, int64_t N, int64_t K, void* c,
-                    int c_dtype, int64_t ldc, void* stream) {
-  int st = check_gemm(a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, M, N, K, c, c_dtype, ldc);
+                    const void* s_b, int64_t ldb, int recipe, int layout, int64_t M, int64_t N, int64_t K,
+                    void* c, int c_dtype, int64_t ldc, void* stream) {
+  int st = check_gemm(a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, layout, M, N, K, c, c_dtype, ldc);
   if (st != FP8MI_OK) return st;
   if (M == 0 || N == 0) return FP8MI_OK;
   fp8mi::GemmParams p{a, fmt_a, s_a, lda, b, fmt_b, s_b, ldb, recipe, M, N, K, c, c_dtype, ldc};
@@ -155,6 +154,6 @@ const char* fp8_status_string(int status) {
   return "unknown status";
 }
 
-int fp8_version(void) { return 400; }
+int fp8_version(void) { return 500; }
 
 }  // extern "C"

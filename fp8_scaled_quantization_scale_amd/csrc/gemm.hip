@@ -611,21 +611,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_kernel(GArgs p
   }  // tile loop
 }
 
-// compute units of the current device (queried once per process and device)
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-
-
 template <int FA, int FB, int REC, int OUT>
 hipError_t launch4(const GemmParams& g, hipStream_t st) {
   using C = TileCfg<REC>;
@@ -649,7 +634,7 @@ hipError_t launch4(const GemmParams& g, hipStream_t st) {
   a.tiles_n = (int)((g.N + BN - 1) / BN);
   // persistent grid: one workgroup per compute unit (the LDS ring admits one)
   const unsigned tiles = (unsigned)a.tiles_m * (unsigned)a.tiles_n;
-  const unsigned cus = (unsigned)cu_count();
+  const unsigned cus = (unsigned)cu_count(stream_device(st));
   const unsigned blocks = tiles < cus ? tiles : cus;
   gemm_kernel<FA, FB, REC, OUT, BM, BN, WAVES_M, WAVES_N, STAGES>
       <<<blocks, 64 * WAVES_M * WAVES_N, 0, st>>>(a);

@@ -32,8 +32,11 @@ __global__ __launch_bounds__(kHistThreads) void history_kernel(float* ring, int3
   uint32_t* slots = reinterpret_cast<uint32_t*>(amax);
   const int t = threadIdx.x;
   // head, slots and ring are all loaded in one round (no load waits on
-  // another); the entry at head is picked out afterwards
-  const int h = *head;
+  // another); the entry at head is picked out afterwards.  A head outside
+  // [0, len) (state saved with another length, or corrupted) is taken
+  // modulo len, so every ring access stays inside the ring.
+  const int h0 = *head % len;
+  const int h = h0 < 0 ? h0 + len : h0;
   // the step's amax: NaN-dominant max over the slots (|x| bit patterns)
   uint32_t k = 0;
   for (int i = t; i < kAmaxSlots; i += kHistThreads) {

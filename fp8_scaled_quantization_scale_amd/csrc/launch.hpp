@@ -5,7 +5,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp8mi {
+
+// ---- the device a launch runs on, and its size -------------------------
+// Work goes to the caller's stream, whose device need not be the current
+// one; persistent grids are sized for that device (a partitioned GPU
+// exposes devices with fewer compute units).
+constexpr int kMaxDevices = 64;
+
+inline int stream_device(hipStream_t st) {
+  int dev = -1;
+  if (st != nullptr && hipStreamGetDevice(st, &dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) return dev;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  return dev;
+}
+
+// Compute units of device `dev`, queried once per process and device.  The
+// cache is atomic: concurrent first calls store the same value.
+inline int cu_count(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // values mirror the FP8MI_* macros of the public header
 constexpr int kInBf16 = 0, kInFp32 = 1;

@@ -41,19 +41,6 @@ constexpr int kThreads = 256;
 // 16-byte alignment and spreads the column writes of a wave over the banks
 constexpr int kCodeStride = 144;
 
-// compute units of the current device (queried once per process and device)
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 // ROW codes are written whole-line by consecutive lanes and not read again
 // by this pass, so they are stored non-temporally (measured on MI355X: an
 // 8192x4096 ROW cast 20.9 -> 18.6 us).  Non-temporal loads of the input and
@@ -749,29 +736,28 @@ __global__ __launch_bounds__(kThreads) void chan_finalize_kernel(float* s_row, i
   if (chan_bad(v) && nonfinite) atomicAdd(nonfinite, 1);
 }
 
-// Persistent grid: as many workgroups as stay resident (per the kernel's
-// register / LDS occupancy), rounded so every workgroup walks the same number
-// of tiles.
+// Persistent grid: as many workgroups as stay resident on the stream's device
+// (per the kernel's register / LDS occupancy, which depends only on the
+// kernel and the architecture), rounded so every workgroup walks the same
+// number of tiles.
 template <typename Kernel>
-unsigned persistent_grid(Kernel k, int64_t tiles, int* cache) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int per_cu = cache[dev];
+unsigned persistent_grid(Kernel k, int64_t tiles, std::atomic<int>& per_cu_cache, hipStream_t st) {
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess || per_cu <= 0)
       per_cu = 1;
-    cache[dev] = per_cu;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
-  const int64_t resident = (int64_t)cu_count() * per_cu;
+  const int64_t resident = (int64_t)cu_count(stream_device(st)) * per_cu;
   const int64_t rounds = (tiles + resident - 1) / resident;
   return (unsigned)((tiles + rounds - 1) / rounds);
 }
 
 template <typename InT, int FMT, int MODE, bool ROW, bool COL, bool CURRENT>
 hipError_t launch_tile_k(const TileArgs& a, int64_t tiles, hipStream_t st) {
-  static int occupancy[64] = {0};  // workgroups per CU, per device
+  static std::atomic<int> occupancy{0};  // workgroups per CU
   auto k = quant_tile_kernel<InT, FMT, MODE, ROW, COL, CURRENT>;
-  unsigned grid = persistent_grid(k, tiles, occupancy);
+  unsigned grid = persistent_grid(k, tiles, occupancy, st);
   // delayed scaling: one accumulator slot per workgroup
   if (MODE == MODE_TENSOR && !CURRENT && grid > (unsigned)kAmaxSlots) grid = kAmaxSlots;
   k<<<grid, kThreads, 0, st>>>(a);
@@ -796,7 +782,7 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
       if (p.rows > 0 && p.cols > 0) {
         const InT* x = reinterpret_cast<const InT*>(p.x);
         uint32_t* slots = reinterpret_cast<uint32_t*>(p.amax) + 1;  // amax[1 .. kAmaxSlots - 1]
-        int64_t cap = (int64_t)cu_count() * 8;
+        int64_t cap = (int64_t)cu_count(stream_device(st)) * 8;
         cap = cap < kAmaxSlots - 1 ? cap : kAmaxSlots - 1;
         int64_t parts;
         if (p.ld_x == p.cols || p.rows == 1) {

@@ -101,6 +101,13 @@ extern "C" {
 #define FP8MI_GEMM_BLOCK_128x128_128x128 4 /* s_a [ceil(M/128) x ceil(K/128)], s_b [ceil(N/128) x ceil(K/128)] */
 #define FP8MI_GEMM_CHANNEL 5             /* s_a [M], s_b [N]: one float per row of A and of B  */
 
+/* GEMM operand layouts [P1 sec. 3.1: fprop, dgrad and wgrad read the same
+ * tensors in different orientations; P3 strategy 3: a block-scaled operand
+ * used transposed is re-quantized, so every GEMM can read codes whose
+ * contraction index is contiguous].  fp8_quantize writes both orientations
+ * (ROW_AND_COL), hence one layout serves all three GEMMs. */
+#define FP8MI_LAYOUT_TN 0 /* a [M x K] and b [N x K], row-major, K contiguous in both */
+
 /* Floats in the amax array of a per-tensor cast.  Each workgroup of a
  * TENSOR_DELAYED cast max-accumulates into a slot of its own with plain
  * loads and stores, and fp8_amax_history_update folds the slots into the
@@ -160,7 +167,9 @@ extern "C" {
  *        channel and block recipes; those blocks use s = 1, MX byte 0xFF).
  * x must not overlap any output.
  * Alignment: x, q_row, q_col 16-byte aligned; ld_x * sizeof(elem),
- * ld_q_row and ld_q_col multiples of 16 bytes.  rows == 0 or cols == 0 is
+ * ld_q_row and ld_q_col multiples of 16 bytes.  Sizes: CHANNEL needs
+ * ceil(rows/128) * ceil(cols/128) < 2^31 (else FP8MI_ERR_UNSUPPORTED); the
+ * other recipes take any size.  rows == 0 or cols == 0 is
  * allowed (CURRENT then writes amax = 0, scale = scale_inv = 1).
  * Returns FP8MI_OK or an FP8MI_ERR_* code; nothing is launched on error. */
 int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
@@ -178,9 +187,9 @@ int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t
  *   amax     : float[FP8MI_AMAX_SLOTS], the accumulator that fp8_quantize
  *              with TENSOR_DELAYED filled since the previous update; its
  *              largest slot is the step's amax a; every slot is reset to 0.
- *   If a is finite it is written to history[*head] and
- *   head = (head + 1) % len; otherwise *nonfinite += 1 and nothing is
- *   pushed.  Then scale = s(max(history)), scale_inv = fl32(1 / scale).
+ *   If a is finite it is written to history[h] and head = (h + 1) % len,
+ *   with h = *head reduced modulo len into [0, len); otherwise
+ *   *nonfinite += 1 and nothing is pushed.  Then scale = s(max(history)), scale_inv = fl32(1 / scale).
  *   len in [1, 65536]; margin in [0, 64].  One workgroup; device state only. */
 int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* amax, int fmt,
                             int margin, float* scale, float* scale_inv, int32_t* nonfinite,
@@ -191,6 +200,8 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  *  quantized inputs with BF16/FP32 outputs; P3 Fig. 1 discussion: per-block
  *  scale factors are applied inside the GEMM]
  *
+ *   layout   : FP8MI_LAYOUT_TN (the only layout built; any other value
+ *              returns FP8MI_ERR_UNSUPPORTED before any launch):
  *   a [M x K] codes (fmt_a), lda; b [N x K] codes (fmt_b), ldb; both with
  *   the contraction index K contiguous.  c [M x N] (c_dtype), ldc.
  *   s_a, s_b : dequantisation scales laid out per `recipe` (see FP8MI_GEMM_*;
@@ -207,15 +218,18 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  *   128-deep block with s_a[i / 128][kb] * s_b[j / 128][kb]; CHANNEL
  *   scales the FP32 result by s_a[i] * s_b[j] (the rows of a and b are the
  *   channels: a per-row scale of X and a per-output-channel scale of W).
+ *   Non-finite inputs follow IEEE arithmetic: a NaN code (E4M3 0x7F/0xFF,
+ *   E5M2 0x7D-0x7F/0xFD-0xFF), an E5M2 infinity (0x7C/0xFC) or an E8M0 NaN
+ *   scale (0xFF) gives the NaN or infinity of the float64 reference.
  * Requirements: M, N, K >= 0; K % 16 == 0; a, b 16-byte aligned,
  * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 and
  * ceil(M/256) * ceil(N/256) < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N.
- * K == 0 writes zeros.
+ * c must not overlap a, b or the scales.  K == 0 writes zeros.
  * Tolerance vs a float64 reference over the dequantized operands:
  * |C - C_ref| <= 2^-10 sum_k |a b| (+ 2^-8 |C_ref| for BF16 output). */
 int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,
                     const uint8_t* b, int fmt_b, const void* s_b, int64_t ldb,
-                    int recipe, int64_t M, int64_t N, int64_t K,
+                    int recipe, int layout, int64_t M, int64_t N, int64_t K,
                     void* c, int c_dtype, int64_t ldc, void* stream);
 
 /* fp8_bf16_gemm -- C = A . B^T with BF16 operands and FP32 accumulation:

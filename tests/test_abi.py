@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (fp8_\w+)$", out, flags=re.M))
     assert set(_declared()) <= exported
-    assert fm.version() == 400
+    assert fm.version() == 500
     assert fm.status_string(fm.ERR_ALIGN).startswith("pointer")
 
 
@@ -77,7 +77,7 @@ def _q(**kw):
     (dict(recipe=fm.TENSOR_CURRENT), fm.ERR_NULL),
     (dict(recipe=fm.TENSOR_CURRENT, amax=GOOD, scale=GOOD), fm.ERR_NULL),
     (dict(recipe=fm.TENSOR_DELAYED, amax=GOOD), fm.ERR_NULL),
-    (dict(rows=65536 * 128), fm.ERR_UNSUPPORTED),
+    (dict(recipe=fm.CHANNEL, rows=(1 << 31) * 128, cols=256, ld_x=256), fm.ERR_UNSUPPORTED),
 ])
 def test_quantize_validation(kw, code):
     assert _q(**kw) == code
@@ -90,8 +90,8 @@ def test_quantize_empty_is_ok_without_launch():
 
 def _g(**kw):
     args = dict(a=GOOD, fmt_a=fm.E4M3, s_a=GOOD, lda=256, b=GOOD, fmt_b=fm.E4M3, s_b=GOOD, ldb=256,
-                recipe=fm.GEMM_TENSOR, M=128, N=128, K=256, c=GOOD, c_dtype=fm.OUT_BF16, ldc=128,
-                stream=0)
+                recipe=fm.GEMM_TENSOR, layout=fm.LAYOUT_TN, M=128, N=128, K=256, c=GOOD,
+                c_dtype=fm.OUT_BF16, ldc=128, stream=0)
     args.update(kw)
     return fm.fp8_gemm_scaled(**args)
 
@@ -112,6 +112,9 @@ def _g(**kw):
     (dict(ldb=264 - 4), fm.ERR_ALIGN),
     (dict(lda=(1 << 22) + 16), fm.ERR_UNSUPPORTED),
     (dict(M=0x7FFFFFFF, N=0x7FFFFFFF, ldc=0x7FFFFFFF), fm.ERR_UNSUPPORTED),  # tile count past 2^31
+    (dict(layout=1), fm.ERR_UNSUPPORTED),  # only the K-contiguous (TN) layout is built
+    (dict(layout=-1), fm.ERR_UNSUPPORTED),
+    (dict(layout=1, a=None, fmt_a=9), fm.ERR_UNSUPPORTED),  # checked first, before anything else
 ])
 def test_gemm_validation(kw, code):
     assert _g(**kw) == code
@@ -173,5 +176,40 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(fm.Fp8Error, match="device tensor"):
         fm.bf16_gemm(x, x)
     with pytest.raises(fm.Fp8Error, match="device tensors"):
-        fm.fp8_gemm_scaled(q, fm.E4M3, s1, 16, q, fm.E4M3, s1, 16, fm.GEMM_TENSOR, 4, 4, 16,
+        fm.fp8_gemm_scaled(q, fm.E4M3, s1, 16, q, fm.E4M3, s1, 16, fm.GEMM_TENSOR, fm.LAYOUT_TN, 4, 4, 16,
                            torch.zeros(4, 4), fm.OUT_FP32, 4, stream=0)
+
+
+# ---------------------------------------------------------------------------
+# the measurement library (libfp8mi_probe.so, include/fp8mi_probe.h)
+# ---------------------------------------------------------------------------
+
+PROBE_HEADER = os.path.join(ROOT, "include", "fp8mi_probe.h")
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from fp8_scaled_quantization_scale_amd import probe
+
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"^\s*\w+\**\s+\**(fp8probe_\w+)\s*\(", text, flags=re.M)))
+    assert declared == sorted(probe.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True, text=True).stdout
+    assert set(declared) <= set(re.findall(r" T (fp8probe_\w+)$", out, flags=re.M))
+    defs = dict(re.findall(r"^#define FP8PROBE_(\w+) (\d+)", open(PROBE_HEADER).read(), flags=re.M))
+    assert {k: int(v) for k, v in defs.items()} == {"READ": probe.READ, "COPY": probe.COPY, "HALF": probe.HALF,
+                                                     "SPLIT": probe.SPLIT}
+
+
+def test_probe_validation():
+    from fp8_scaled_quantization_scale_amd import probe
+
+    lib = probe.load()
+    assert lib.fp8probe_stream(GOOD, 64, GOOD, None, 9, None) == -2
+    assert lib.fp8probe_stream(GOOD, 63, GOOD, GOOD, probe.HALF, None) == -3
+    assert lib.fp8probe_stream(GOOD, -1, GOOD, None, probe.COPY, None) == -3
+    assert lib.fp8probe_stream(None, 64, GOOD, None, probe.COPY, None) == -1
+    assert lib.fp8probe_stream(GOOD, 64, GOOD, None, probe.SPLIT, None) == -1
+    assert lib.fp8probe_stream(GOOD + 8, 64, GOOD, None, probe.COPY, None) == -5
+    assert lib.fp8probe_stream(GOOD, 0, GOOD, None, probe.READ, None) == 0
+    assert lib.fp8probe_mfma(0, 4, GOOD, GOOD, None) == -3
+    assert lib.fp8probe_mfma(10, 4, None, GOOD, None) == -1

@@ -4,7 +4,7 @@ bench.py times (its Step, one input copy, one step).
 Quantization: codes and scales bit for bit on sampled rows, sampled columns
 of the transposed layouts and sampled 128x128 tile rows / columns; per-tensor
 amax, scales and the delayed-scaling history step checked on whole tensors.
-GEMMs: every entry of two corner 128x128 output tiles and of a cross of ~66
+GEMMs: every entry of the four corner 128x128 output tiles and of a cross of ~66
 random rows x ~66 random columns, within |C - C_ref| <= 2^-10 S + 2^-8 |C_ref|
 (BF16 output), C_ref and S from the oracle in float64 on the GPU's own codes
 and scales (per-tensor scales from the oracle's own amax)."""
@@ -56,7 +56,7 @@ def check_gemm(c, deq_a, deq_b, M, N, tag):
     got = c[_ix(c, I)][:, _ix(c, J)].float().cpu().numpy()
     bad = oracle.gemm_violations(got, cref, s, "bf16")
     assert not bad.any(), (tag, "cross", int(bad.sum()))
-    for r0, c0 in ((0, 0), (M - 128, N - 128)):
+    for r0, c0 in ((0, 0), (0, N - 128), (M - 128, 0), (M - 128, N - 128)):
         ri, cj = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
         cref, s = oracle.gemm_ref(deq_a(ri), deq_b(cj))
         got = c[r0:r0 + 128, c0:c0 + 128].float().cpu().numpy()

@@ -141,7 +141,7 @@ def test_exact_small_integer_products(recipe):
 def test_k_zero_writes_zeros():
     need_gpu()
     c = torch.full((40, 50), 7.0, dtype=torch.float32, device="cuda")
-    st = fm.fp8_gemm_scaled(None, fm.E4M3, None, 16, None, fm.E4M3, None, 16, fm.GEMM_TENSOR,
+    st = fm.fp8_gemm_scaled(None, fm.E4M3, None, 16, None, fm.E4M3, None, 16, fm.GEMM_TENSOR, fm.LAYOUT_TN,
                             40, 50, 0, c, fm.OUT_FP32, 50)
     assert st == fm.OK
     assert torch.count_nonzero(c).item() == 0

@@ -46,9 +46,9 @@ class StepBuffers:
         ok(fm.fp8_quantize(self.G, fm.IN_BF16, M, N, N, fm.TENSOR_DELAYED, fm.E5M2, fm.ROW, 0,
                            self.qg, N, None, None, 0, None, st.scale, None, st.amax, st.nonfinite))
         ok(fm.fp8_gemm_scaled(self.qx, fm.E4M3, self.six, K, self.qw, fm.E4M3, self.siw, K,
-                              fm.GEMM_TENSOR, M, N, K, self.y, fm.OUT_BF16, N))
+                              fm.GEMM_TENSOR, fm.LAYOUT_TN, M, N, K, self.y, fm.OUT_BF16, N))
         ok(fm.fp8_gemm_scaled(self.qg, fm.E5M2, st.scale_inv, N, self.qwt, fm.E4M3, self.siw, N,
-                              fm.GEMM_TENSOR, M, K, N, self.dx, fm.OUT_BF16, K))
+                              fm.GEMM_TENSOR, fm.LAYOUT_TN, M, K, N, self.dx, fm.OUT_BF16, K))
         ok(fm.fp8_amax_history_update(st.history, st.head, 200, st.amax, fm.E5M2, 0,
                                       st.scale, st.scale_inv, st.nonfinite))
 

@@ -2,7 +2,8 @@
 
 fp8_gemm_scaled takes K and leading dimensions up to 2^22 bytes (operand
 panels are addressed with 32-bit buffer offsets: 256 rows x 2^22 = 2^30),
-and fp8_quantize up to 65535 tiles of 128 rows.  These tests run those
+and fp8_quantize over more than 65535 tiles of 128 rows (a 1-D persistent
+grid: no row-tile limit).  These tests run those
 extremes and compare sampled outputs with the oracle: GEMM entries against
 the float64 dot product of the dequantized rows (random operand codes with
 random signs, so the FP32 accumulation error stays far inside the
@@ -78,10 +79,11 @@ def test_gemm_at_the_largest_k(recipe):
 
 
 @pytest.mark.parametrize("recipe", [fm.BLOCK_1x128, fm.MX_1x32, fm.TENSOR_CURRENT])
-def test_quantize_at_the_most_row_tiles(recipe):
-    """65535 tiles of 128 rows (8388480 rows) of 16 columns, both layouts."""
+def test_quantize_past_65535_row_tiles(recipe):
+    """65601 tiles of 128 rows (8396837 rows, the last tile ragged) of 16
+    columns, both layouts."""
     need_gpu()
-    rows, cols = 65535 * 128, 16
+    rows, cols = 65600 * 128 + 37, 16
     x = workloads.make(workloads.Tensor("X", rows, cols, "outliers", 1.0, 81, 0.02, 50.0), "cuda")
     orient = fm.ROW if recipe == fm.TENSOR_CURRENT else fm.ROW_AND_COL
     q = fm.quantize(x, recipe, fm.E4M3, orient)
@@ -104,10 +106,11 @@ def test_quantize_at_the_most_row_tiles(recipe):
     assert np.array_equal(q.s_row[torch.as_tensor(rsel, device="cuda")].cpu().numpy(), og)
     # column blocks along the rows: 128 (1x128) or 32 (MX) rows each
     cb = 128 if recipe == fm.BLOCK_1x128 else 32
-    nblk = rows // cb
-    for blk in (0, nblk - 1, int(rng.integers(0, nblk))):
+    nblk = (rows + cb - 1) // cb
+    for blk in (0, nblk - 2, nblk - 1, int(rng.integers(0, nblk))):
         r0 = blk * cb
-        xb = x[r0:r0 + cb].float().cpu().numpy()
+        r1 = min(rows, r0 + cb)
+        xb = x[r0:r1].float().cpu().numpy()
         oq, og, _ = qfun(xb, cb, 1)
-        assert np.array_equal(q.q_col[:, r0:r0 + cb].cpu().numpy(), oq.T), blk
+        assert np.array_equal(q.q_col[:, r0:r1].cpu().numpy(), oq.T), blk
         assert np.array_equal(q.s_col[:, blk].cpu().numpy(), og[0]), blk

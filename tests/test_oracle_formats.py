@@ -99,6 +99,48 @@ def test_encode_vs_torch_strided_fp32(fmt):
     assert np.array_equal(oracle.encode(fmt, v), _torch_codes(fmt, v))
 
 
+def _sweep_chunk(fmt: str, start: int, n: int) -> int:
+    """Mismatches of the oracle's encoder over the float32 bit patterns
+    [start, start + n): against torch's nearest-even cast where |v| <= max,
+    against saturation to +-max beyond (+-Inf included), and against the
+    canonical NaN code 0x7F for every NaN pattern."""
+    v = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    got = oracle.encode(fmt, v)
+    a = np.abs(v)
+    inr = a <= oracle.max_value(fmt)
+    bad = int(np.count_nonzero(got[inr] != _torch_codes(fmt, np.ascontiguousarray(v[inr]))))
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    over = a > oracle.max_value(fmt)  # NaN compares false: not in `over`
+    want = np.where(np.signbit(v[over]), 0x80 | top, top).astype(np.uint8)
+    bad += int(np.count_nonzero(got[over] != want))
+    nan = np.isnan(v)
+    bad += int(np.count_nonzero(got[nan] != 0x7F))
+    assert int(inr.sum() + over.sum() + nan.sum()) == n
+    return bad
+
+
+@pytest.mark.parametrize("fmt", oracle.FORMATS)
+def test_encode_every_fp32_pattern(fmt):
+    """All 2^32 float32 inputs: the oracle's nearest-value search equals
+    torch's round-to-nearest-even cast (a library routine with its own
+    implementation) everywhere inside the format's range, and the closed-form
+    saturation / NaN rule outside it.  Chunks run on worker threads (the
+    oracle's C loop drops the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    oracle.encode(fmt, np.zeros(1, np.float32))  # fill the oracle's table once
+    chunk = 1 << 24
+    nthreads = min(8, os.cpu_count() or 1)
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with ThreadPoolExecutor(nthreads) as ex:
+            bad = sum(ex.map(lambda c: _sweep_chunk(fmt, c * chunk, chunk), range((1 << 32) // chunk)))
+    finally:
+        torch.set_num_threads(torch_threads)
+    assert bad == 0
+
+
 @pytest.mark.parametrize("fmt", oracle.FORMATS)
 def test_encode_vs_torch_all_bf16(fmt):
     mx = oracle.max_value(fmt)

@@ -39,8 +39,8 @@ AMAX_SLOTS = 1024  # floats in the amax array of a per-tensor cast
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
 TORCH_FP8 = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
 
-EXPORTS = ("fp8_quantize", "fp8_amax_history_update", "fp8_gemm_scaled", "fp8_bf16_gemm",
-           "fp8_status_string", "fp8_version")
+EXPORTS = ("fp8_quantize", "fp8_quantize_static_scratch", "fp8_amax_history_update", "fp8_gemm_scaled",
+           "fp8_bf16_gemm", "fp8_status_string", "fp8_version")
 
 
 class Fp8Error(RuntimeError):
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH):
     lib.fp8_quantize.restype = i32
     lib.fp8_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, i32,
                                  vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp]
+    lib.fp8_quantize_static_scratch.restype = i32
+    lib.fp8_quantize_static_scratch.argtypes = lib.fp8_quantize.argtypes
     lib.fp8_amax_history_update.restype = i32
     lib.fp8_amax_history_update.argtypes = [vp, vp, i64, vp, i32, i32, vp, vp, vp, vp]
     lib.fp8_gemm_scaled.restype = i32
@@ -138,6 +140,16 @@ def fp8_quantize(x, x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin,
     return load().fp8_quantize(_p(x), x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin,
                                _p(q_row), ld_q_row, _p(s_row), _p(q_col), ld_q_col, _p(s_col),
                                _p(scale), _p(scale_inv), _p(amax), _p(nonfinite), _stream(stream))
+
+
+def fp8_quantize_static_scratch(x, x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin,
+                                q_row, ld_q_row, s_row, q_col, ld_q_col, s_col,
+                                scale, scale_inv, amax, nonfinite, stream=None) -> int:
+    """fp8_quantize with current scaling's partial maxima in the library's
+    static device scratch (amax: one float for TENSOR_CURRENT)."""
+    return load().fp8_quantize_static_scratch(_p(x), x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin,
+                                              _p(q_row), ld_q_row, _p(s_row), _p(q_col), ld_q_col, _p(s_col),
+                                              _p(scale), _p(scale_inv), _p(amax), _p(nonfinite), _stream(stream))
 
 
 def fp8_amax_history_update(history, head, length, amax, fmt, margin, scale, scale_inv,

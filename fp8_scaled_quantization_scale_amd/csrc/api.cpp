@@ -101,6 +101,20 @@ int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t
   return hip_status(fp8mi::launch_quantize(p, (hipStream_t)stream));
 }
 
+int fp8_quantize_static_scratch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int recipe,
+                                int fmt, int orient, int margin, uint8_t* q_row, int64_t ld_q_row, void* s_row,
+                                uint8_t* q_col, int64_t ld_q_col, void* s_col, float* scale, float* scale_inv,
+                                float* amax, int32_t* nonfinite, void* stream) {
+  int st = check_quantize(x, x_dtype, rows, cols, ld_x, recipe, fmt, orient, margin, q_row, ld_q_row,
+                          s_row, q_col, ld_q_col, s_col, scale, scale_inv, amax);
+  if (st != FP8MI_OK) return st;
+  if ((rows == 0 || cols == 0) && recipe != FP8MI_TENSOR_CURRENT) return FP8MI_OK;
+  fp8mi::QuantParams p{x,      x_dtype,  rows,  cols,  ld_x,     recipe, fmt,      orient, margin,
+                       q_row,  ld_q_row, s_row, q_col, ld_q_col, s_col,  scale,    scale_inv,
+                       amax,   nonfinite};
+  return hip_status(fp8mi::launch_quantize_static_scratch(p, (hipStream_t)stream));
+}
+
 int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* amax, int fmt, int margin,
                             float* scale, float* scale_inv, int32_t* nonfinite, void* stream) {
   if (fmt != FP8MI_E4M3 && fmt != FP8MI_E5M2) return FP8MI_ERR_ENUM;

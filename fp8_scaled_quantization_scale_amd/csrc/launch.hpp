@@ -61,6 +61,9 @@ struct QuantParams {
   float* scale_inv;
   float* amax;
   int32_t* nonfinite;
+  // current scaling: where the amax pass leaves its per-workgroup partial
+  // maxima (nullptr: amax[1 ..], the caller's array)
+  uint32_t* partials = nullptr;
 };
 
 struct GemmParams {
@@ -80,6 +83,9 @@ struct GemmParams {
 };
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t st);
+// fp8_quantize with current scaling's partial maxima in the library's static
+// device scratch instead of amax[1 ..] (see quantize.hip)
+hipError_t launch_quantize_static_scratch(const QuantParams& p, hipStream_t st);
 hipError_t launch_empty_scale(float* amax, float* scale, float* scale_inv, hipStream_t st);
 hipError_t launch_history(float* history, int32_t* head, int len, float* amax, int fmt, int margin,
                           float* scale, float* scale_inv, int32_t* nonfinite, hipStream_t st);

@@ -28,6 +28,9 @@
 // combines results across workgroups with atomics: on MI355X atomics on one
 // address serialise (about 14 ns each), which for a thousand workgroups
 // costs as much as the whole cast.
+#include <atomic>
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -37,6 +40,9 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+// partial maxima of current scaling's amax pass: one per workgroup, at most
+// this many whatever the tensor's size (the pass grid-strides)
+constexpr int kMaxPartials = kAmaxSlots - 1;
 // byte stride of the transposed code tile staged in LDS: 144 = 128 + 16 keeps
 // 16-byte alignment and spreads the column writes of a wave over the banks
 constexpr int kCodeStride = 144;
@@ -154,10 +160,11 @@ struct TileArgs {
   void* s_col;
   float* scale;       // per-tensor: in (delayed) / out (current)
   float* scale_inv;   // per-tensor current: out
-  float* amax;        // per-tensor: out amax[0] + partial slots amax[1..] (current) / slot accumulator (delayed)
+  float* amax;        // per-tensor: out amax[0] (current) / slot accumulator (delayed)
   int32_t* nonfinite;
   int margin;
-  int nparts;         // current: partial maxima in amax[1 .. nparts]
+  int nparts;         // current: partial maxima in parts[0 .. nparts - 1]
+  const uint32_t* parts;
 };
 
 // max |x| key of 8 BF16 values packed in a uint4: packed 16-bit max of the
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(TileArgs a) {
     if constexpr (CURRENT) {
       // every workgroup folds the amax pass's partial maxima (a few KB, from
       // L2); none of them writes the slots, so there is no ordering to keep
-      const uint32_t* slots = reinterpret_cast<const uint32_t*>(a.amax) + 1;
+      const uint32_t* slots = a.parts;
       uint32_t k = 0;
       for (int i = tid; i < a.nparts; i += kThreads) k = k > slots[i] ? k : slots[i];
       const float am = key_to_float(wg_max_u32(k, red4));
@@ -765,9 +772,9 @@ hipError_t launch_tile_k(const TileArgs& a, int64_t tiles, hipStream_t st) {
 }
 
 template <typename InT, int FMT, int MODE, bool CURRENT>
-hipError_t launch_tile(const QuantParams& p, hipStream_t st, int nparts = 0) {
+hipError_t launch_tile(const QuantParams& p, hipStream_t st, int nparts = 0, const uint32_t* parts = nullptr) {
   TileArgs a{p.x, p.rows, p.cols, p.ld_x, p.q_row, p.ld_q_row, p.s_row, p.q_col, p.ld_q_col,
-             p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin, nparts};
+             p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin, nparts, parts};
   const int64_t tiles = ((p.cols + kTile - 1) / kTile) * ((p.rows + kTile - 1) / kTile);
   const bool row = p.orient & 1, col = p.orient & 2;
   if (row && col) return launch_tile_k<InT, FMT, MODE, true, true, CURRENT>(a, tiles, st);
@@ -781,9 +788,10 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
     case kRecipeTensorCurrent: {
       if (p.rows > 0 && p.cols > 0) {
         const InT* x = reinterpret_cast<const InT*>(p.x);
-        uint32_t* slots = reinterpret_cast<uint32_t*>(p.amax) + 1;  // amax[1 .. kAmaxSlots - 1]
+        // partial maxima: amax[1 .. kAmaxSlots - 1], or the static scratch
+        uint32_t* slots = p.partials ? p.partials : reinterpret_cast<uint32_t*>(p.amax) + 1;
         int64_t cap = (int64_t)cu_count(stream_device(st)) * 8;
-        cap = cap < kAmaxSlots - 1 ? cap : kAmaxSlots - 1;
+        cap = cap < kMaxPartials ? cap : kMaxPartials;
         int64_t parts;
         if (p.ld_x == p.cols || p.rows == 1) {
           const int64_t n = p.rows * p.cols;
@@ -804,7 +812,7 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
           amax_kernel<InT><<<dim3((unsigned)gx, (unsigned)gy), kThreads, 0, st>>>(x, p.rows, p.cols, p.ld_x,
                                                                                   slots);
         }
-        return launch_tile<InT, FMT, MODE_TENSOR, true>(p, st, (int)parts);
+        return launch_tile<InT, FMT, MODE_TENSOR, true>(p, st, (int)parts, slots);
       }
       // empty tensor: amax = 0 -> scale = scale_inv = 1
       return launch_empty_scale(p.amax, p.scale, p.scale_inv, st);
@@ -822,7 +830,7 @@ hipError_t launch_fmt(const QuantParams& p, hipStream_t st) {
       return launch_tile<InT, FMT, MODE_MX32F, false>(p, st);
     case kRecipeChannel: {
       TileArgs a{p.x, p.rows, p.cols, p.ld_x, p.q_row, p.ld_q_row, p.s_row, p.q_col, p.ld_q_col,
-                 p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin, 0};
+                 p.s_col, p.scale, p.scale_inv, p.amax, p.nonfinite, p.margin, 0, nullptr};
       const bool row = p.orient & 1, col = p.orient & 2;
       const int64_t tx = (p.cols + kTile - 1) / kTile, ty = (p.rows + kTile - 1) / kTile;
       const unsigned tiles = (unsigned)(tx * ty);
@@ -863,12 +871,55 @@ hipError_t launch_empty_scale(float* amax, float* scale, float* scale_inv, hipSt
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (fp8_quantize_static_scratch):
+// current scaling's partial maxima live in this file-scope device array, one
+// copy per GPU, instead of the caller's amax[1 ..].  Host code never passes
+// the array's name to a kernel: it looks up the array's device address once
+// per device (with that device current) and passes that.  Every slot the
+// cast pass reads is written by the amax pass of the same call first, so the
+// array needs no clearing; calls that overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+constexpr int kScratchWords = 1024;
+static_assert(kMaxPartials <= kScratchWords, "the amax pass's partial maxima fit the scratch");
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+// device address of `scratch` on device dev (nullptr if the lookup failed)
+static uint32_t* scratch_address(int dev) {
+  static std::atomic<uint32_t*> addr[kMaxDevices];
+  static std::mutex lock;
+  uint32_t* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> g(lock);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* found = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&found, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !found) return nullptr;
+  p = static_cast<uint32_t*>(found);
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 hipError_t launch_quantize(const QuantParams& p, hipStream_t st) {
   if (p.recipe != kRecipeTensorCurrent && (p.rows == 0 || p.cols == 0)) return hipSuccess;
   if (p.x_dtype == kInBf16) {
     return p.fmt == kE4M3 ? launch_fmt<uint16_t, kE4M3>(p, st) : launch_fmt<uint16_t, kE5M2>(p, st);
   }
   return p.fmt == kE4M3 ? launch_fmt<float, kE4M3>(p, st) : launch_fmt<float, kE5M2>(p, st);
+}
+
+hipError_t launch_quantize_static_scratch(const QuantParams& p, hipStream_t st) {
+  QuantParams q = p;
+  if (p.recipe == kRecipeTensorCurrent && p.rows > 0 && p.cols > 0) {
+    q.partials = scratch_address(stream_device(st));
+    if (!q.partials) return hipErrorInvalidSymbol;
+  }
+  return launch_quantize(q, st);
 }
 
 }  // namespace fp8mi

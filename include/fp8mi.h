@@ -179,6 +179,26 @@ int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t
                  float* scale, float* scale_inv, float* amax, int32_t* nonfinite,
                  void* stream);
 
+/* fp8_quantize_static_scratch -- fp8_quantize for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, checks, results and errors as
+ * fp8_quantize, with one difference: TENSOR_CURRENT keeps the partial maxima
+ * of its amax pass in a static device array of the library (1024 words =
+ * 4 KB per GPU, allocated when the library is loaded and held until the
+ * process ends) instead of amax[1 ..], so `amax` need hold only amax[0]
+ * (one float).  The pass uses at most 1023 partials whatever the tensor's
+ * size, so no size is refused for want of scratch.  TENSOR_DELAYED still
+ * takes its float[FP8MI_AMAX_SLOTS] accumulator (caller-owned state, not
+ * scratch).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams) race and must be ordered
+ * by the caller; each call writes every slot it reads before reading it. */
+int fp8_quantize_static_scratch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                int recipe, int fmt, int orient, int margin,
+                                uint8_t* q_row, int64_t ld_q_row, void* s_row,
+                                uint8_t* q_col, int64_t ld_q_col, void* s_col,
+                                float* scale, float* scale_inv, float* amax, int32_t* nonfinite,
+                                void* stream);
+
 /* fp8_amax_history_update -- one delayed-scaling step.
  * [P1 sec. 2.1: amax history over the past steps (usually 200), scale from
  *  the maximum of the buffer; P2 sec. 3.3: interval 1 = every step, margin]

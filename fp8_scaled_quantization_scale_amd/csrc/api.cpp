@@ -75,6 +75,8 @@ int check_gemm(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const 
     if (K % 16) return FP8MI_ERR_SHAPE;
     if (lda < K || ldb < K) return FP8MI_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16) return FP8MI_ERR_ALIGN;
+    // scale grids are read in whole aligned dwords (MX rows' E8M0 bytes too)
+    if (((uintptr_t)s_a & 3u) || ((uintptr_t)s_b & 3u)) return FP8MI_ERR_ALIGN;
   }
   if (M > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL) return FP8MI_ERR_UNSUPPORTED;
   // operand panels are addressed with 32-bit buffer offsets
@@ -162,7 +164,7 @@ const char* fp8_status_string(int status) {
     case FP8MI_ERR_ENUM: return "unknown recipe, format, orientation or dtype value";
     case FP8MI_ERR_SHAPE: return "bad size, leading dimension or margin";
     case FP8MI_ERR_UNSUPPORTED: return "valid arguments, but this combination is not supported";
-    case FP8MI_ERR_ALIGN: return "pointer or leading dimension breaks 16-byte alignment";
+    case FP8MI_ERR_ALIGN: return "pointer or leading dimension breaks its alignment (16 bytes; GEMM scales 4)";
     case FP8MI_ERR_HIP: return g_hip_msg;
   }
   return "unknown status";

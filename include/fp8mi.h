@@ -64,7 +64,7 @@ extern "C" {
 #define FP8MI_ERR_ENUM (-2)        /* unknown recipe / format / dtype value */
 #define FP8MI_ERR_SHAPE (-3)       /* negative size, ld too small, margin   */
 #define FP8MI_ERR_UNSUPPORTED (-4) /* valid values, combination not built   */
-#define FP8MI_ERR_ALIGN (-5)       /* pointer or ld breaks 16-byte alignment */
+#define FP8MI_ERR_ALIGN (-5)       /* pointer or ld breaks its alignment     */
 #define FP8MI_ERR_HIP (-6)         /* a HIP launch failed                   */
 
 /* ---- enums ------------------------------------------------------------ */
@@ -242,6 +242,8 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  *   E5M2 0x7D-0x7F/0xFD-0xFF), an E5M2 infinity (0x7C/0xFC) or an E8M0 NaN
  *   scale (0xFF) gives the NaN or infinity of the float64 reference.
  * Requirements: M, N, K >= 0; K % 16 == 0; a, b 16-byte aligned,
+ * s_a, s_b 4-byte aligned (scale grids are read in aligned dwords; for MX
+ * that may touch up to 3 bytes past a grid's last row, never used),
  * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 and
  * ceil(M/256) * ceil(N/256) < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N.
  * c must not overlap a, b or the scales.  K == 0 writes zeros.

@@ -110,6 +110,8 @@ def _g(**kw):
     (dict(ldc=100), fm.ERR_SHAPE),
     (dict(a=GOOD + 1), fm.ERR_ALIGN),
     (dict(ldb=264 - 4), fm.ERR_ALIGN),
+    (dict(s_a=GOOD + 2), fm.ERR_ALIGN),  # scale grids are read in aligned dwords
+    (dict(s_b=GOOD + 1, recipe=3), fm.ERR_ALIGN),
     (dict(lda=(1 << 22) + 16), fm.ERR_UNSUPPORTED),
     (dict(M=0x7FFFFFFF, N=0x7FFFFFFF, ldc=0x7FFFFFFF), fm.ERR_UNSUPPORTED),  # tile count past 2^31
     (dict(layout=1), fm.ERR_UNSUPPORTED),  # only the K-contiguous (TN) layout is built

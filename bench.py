@@ -500,19 +500,28 @@ def hbm_ceilings(ev: "HipEvents") -> dict:
     at each read:write byte mix: READ, COPY (1:1), ROW (2 bytes in, 1 out: a
     cast writing one code layout) and ROW_AND_COL (2 in, 1 + 1 out: both
     layouts).  1 GiB of source, median of 3 blocks of 3 passes; bytes read +
-    written over the time."""
+    written over the time.  Each mix runs with plain and non-temporal loads
+    and stores, grid-strided and in one contiguous range per workgroup; the
+    best is the ceiling, and `hints` names it."""
     src = torch.empty(CEIL_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     d0 = torch.empty(CEIL_BYTES, dtype=torch.uint8, device="cuda")
     d1 = torch.empty(CEIL_BYTES // 2, dtype=torch.uint8, device="cuda")
-    out = {}
+    out, hints = {}, {}
     for name, mix in MIX_OF.items():
-        ms = _time_ms(lambda: probe.stream(src, d0, d1 if mix == probe.SPLIT else None, mix), 3, ev)
         moved = CEIL_BYTES + {probe.READ: 0, probe.COPY: CEIL_BYTES, probe.HALF: CEIL_BYTES // 2,
                               probe.SPLIT: CEIL_BYTES}[mix]
-        out[name] = round(moved / (ms * 1e-3) / 1e9, 1)
+        for h in range(0, 8 * probe.NT_LOAD, probe.NT_LOAD):  # every subset of the three hint bits
+            if mix == probe.READ and h & probe.NT_STORE:
+                continue
+            hn = "+".join(n for b, n in ((probe.NT_LOAD, "nt_load"), (probe.NT_STORE, "nt_store"),
+                                         (probe.BLOCKED, "blocked")) if h & b) or "plain"
+            ms = _time_ms(lambda: probe.stream(src, d0, d1 if mix == probe.SPLIT else None, mix | h), 3, ev)
+            gbs = round(moved / (ms * 1e-3) / 1e9, 1)
+            if gbs > out.get(name, 0.0):
+                out[name], hints[name] = gbs, hn
     del src, d0, d1
     torch.cuda.empty_cache()
-    return out
+    return {"gbs": out, "hints": hints}
 
 
 def mfma_ceiling(ev: "HipEvents") -> dict:
@@ -787,7 +796,7 @@ def main():
                         "algorithmic_bytes": work})
             mix = "ROW_AND_COL" if "row_col" in name else "ROW"
             if ceil_hbm:
-                ent.update({"ceiling_mix": mix, "frac_hbm_ceiling": round(gbs / ceil_hbm[mix], 4)})
+                ent.update({"ceiling_mix": mix, "frac_hbm_ceiling": round(gbs / ceil_hbm["gbs"][mix], 4)})
         kernels[name] = ent
 
     value = step.gemm_flops() / (ms_step * 1e-3) / 1e12
@@ -813,9 +822,10 @@ def main():
         "event_pair_empty_us": round(float(np.median(empty)), 2),
         "kernels": kernels,
         "mfma_ceiling": ceil_mfma if not args.no_probes else None,
-        "hbm_ceiling": ({"gbs": ceil_hbm, "source_bytes": CEIL_BYTES,
-                         "note": "in-tree streams (libfp8mi_probe.so): bytes read + written / time; ROW = 2 bytes "
-                                 "in, 1 out; ROW_AND_COL = 2 in, 1 + 1 out"} if ceil_hbm else None),
+        "hbm_ceiling": ({"gbs": ceil_hbm["gbs"], "hints": ceil_hbm["hints"], "source_bytes": CEIL_BYTES,
+                         "note": "in-tree streams (libfp8mi_probe.so), best of plain / non-temporal loads and "
+                                 "stores, strided / blocked: bytes read + written / time; ROW = 2 bytes in, 1 out; ROW_AND_COL = 2 "
+                                 "in, 1 + 1 out"} if ceil_hbm else None),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -502,6 +502,21 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     // ---- prologue: steps 0 and 1 whole, each wave its own DMA set of each
     if (0 < KT) issue(0);
     if (1 < KT) issue(1);
+    // channel scaling: the lane's row and column scales, fetched now so that
+    // a short K loop does not end waiting on them
+    const int cbase = n0 + wn * kWN + lg * kCPL;  // first of the lane's CPL output columns
+    float csa[REC == kGemmChannel ? kMT : 1], csb[REC == kGemmChannel ? kCPL : 1];
+    if constexpr (REC == kGemmChannel) {
+      const float* sap = reinterpret_cast<const float*>(p.sa);
+      const float* sbp = reinterpret_cast<const float*>(p.sb);
+#pragma unroll
+      for (int c = 0; c < kCPL; ++c) csb[c] = (KT > 0 && cbase + c < p.N) ? sbp[cbase + c] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) {
+        const int row = m0 + wm * kWM + i * 16 + lr;
+        csa[i] = (KT > 0 && row < p.M) ? sap[row] : 0.0f;
+      }
+    }
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -538,24 +553,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     }
     constexpr int ESIZE = OUT == kOutBf16 ? 2 : 4;
     const bool vec_ok = ((p.ldc * ESIZE) % 16 == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
-    const int cbase = n0 + wn * kWN + lg * kCPL;
-    float csb[REC == kGemmChannel ? kCPL : 1];
-    if constexpr (REC == kGemmChannel) {
-      const float* sbp = reinterpret_cast<const float*>(p.sb);
-#pragma unroll
-      for (int c = 0; c < kCPL; ++c) csb[c] = (KT > 0 && cbase + c < p.N) ? sbp[cbase + c] : 0.0f;
-    }
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
       const int row = m0 + wm * kWM + i * 16 + lr;
       if (row >= p.M) continue;
       float v[kCPL];
       if constexpr (REC == kGemmChannel) {
-        const float sar = KT > 0 ? reinterpret_cast<const float*>(p.sa)[row] : 0.0f;
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[4 * j + r] = acc[i][j][r] * (sar * csb[4 * j + r]);
+          for (int r = 0; r < 4; ++r) v[4 * j + r] = acc[i][j][r] * (csa[i] * csb[4 * j + r]);
       } else {
 #pragma unroll
         for (int j = 0; j < kNT; ++j)

@@ -16,68 +16,101 @@ constexpr int kStreamThreads = 256;
 constexpr int kMfmaWaves = 8;  // two waves per SIMD
 constexpr int kMfmaAcc = 8;    // independent products in flight per wave
 
+constexpr int kMfmaLdsWords = 96 * 1024 / 4;  // one workgroup per compute unit
+
 __device__ __forceinline__ uint4 xor4(uint4 a, uint4 b) { return make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w); }
 
-// Every access is at an index below its bound (n for src, n or n / 2 for
-// dst0 / dst1): the loop conditions check the largest index of each trip.
-template <int MIX>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st(uint4* p, uint4 v) {
+  if constexpr (NT) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  } else {
+    *p = v;
+  }
+}
+
+// Work item i of a pass reads src[i] (READ, COPY) or src[2i], src[2i+1]
+// (HALF, SPLIT) and writes its output chunk(s) at i; there are n items (READ,
+// COPY) or n / 2.  Grid-strided: thread t of workgroup b takes items
+// b * 256 + t + k * (grid * 256).  BLOCKED: workgroup b takes the contiguous
+// range [b * per, (b + 1) * per) of items, thread t every 256th of it.
+// Eight 16-byte loads are in flight per thread per trip.  Every access is at
+// an index below its bound (n for src, n or n / 2 for dst0 / dst1): each
+// trip's largest item index is checked against the item count.
+template <int MIX, bool NTL, bool NTS, bool BLOCKED>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const uint4* __restrict__ src, int64_t n,
                                                                 uint4* __restrict__ dst0, uint4* __restrict__ dst1) {
-  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-  int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
-  if constexpr (MIX == FP8PROBE_READ || MIX == FP8PROBE_COPY) {
-    uint4 acc = make_uint4(0, 0, 0, 0);
-    for (; i + 3 * stride < n; i += 4 * stride) {
-      const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-      if constexpr (MIX == FP8PROBE_COPY) {
-        dst0[i] = a;
-        dst0[i + stride] = b;
-        dst0[i + 2 * stride] = c;
-        dst0[i + 3 * stride] = d;
-      } else {
-        acc = xor4(acc, xor4(xor4(a, b), xor4(c, d)));
-      }
-    }
-    for (; i < n; i += stride) {
-      const uint4 a = src[i];
-      if constexpr (MIX == FP8PROBE_COPY) dst0[i] = a;
-      else acc = xor4(acc, a);
-    }
-    if constexpr (MIX == FP8PROBE_READ) {
-      if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0xF39CC060u && acc.w == 0x5CEDC834u) dst0[0] = acc;
-    }
+  constexpr bool kPair = MIX == FP8PROBE_HALF || MIX == FP8PROBE_SPLIT;
+  constexpr int U = kPair ? 4 : 8;  // items per trip (8 loads either way)
+  const int64_t items = kPair ? n / 2 : n;
+  int64_t i, end, step;
+  if constexpr (BLOCKED) {
+    const int64_t per = (items + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    end = b0 + per < items ? b0 + per : items;
+    i = b0 + threadIdx.x;
+    step = kStreamThreads;
   } else {
-    const int64_t h = n / 2;  // output chunks
-    for (; i + 3 * stride < h; i += 4 * stride) {
-      uint4 a[4], b[4];
+    end = items;
+    i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    step = (int64_t)gridDim.x * kStreamThreads;
+  }
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (; i + (U - 1) * step < end; i += U * step) {
+    uint4 a[U], b[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = src[2 * (i + u * stride)];
-        b[u] = src[2 * (i + u * stride) + 1];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if constexpr (MIX == FP8PROBE_HALF) {
-          dst0[i + u * stride] = xor4(a[u], b[u]);
-        } else {
-          dst0[i + u * stride] = a[u];
-          dst1[i + u * stride] = b[u];
-        }
-      }
-    }
-    for (; i < h; i += stride) {
-      const uint4 a = src[2 * i], b = src[2 * i + 1];
-      if constexpr (MIX == FP8PROBE_HALF) {
-        dst0[i] = xor4(a, b);
+    for (int u = 0; u < U; ++u) {
+      if constexpr (kPair) {
+        a[u] = ld<NTL>(src + 2 * (i + u * step));
+        b[u] = ld<NTL>(src + 2 * (i + u * step) + 1);
       } else {
-        dst0[i] = a;
-        dst1[i] = b;
+        a[u] = ld<NTL>(src + i + u * step);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (MIX == FP8PROBE_READ) acc = xor4(acc, a[u]);
+      else if constexpr (MIX == FP8PROBE_COPY) st<NTS>(dst0 + i + u * step, a[u]);
+      else if constexpr (MIX == FP8PROBE_HALF) st<NTS>(dst0 + i + u * step, xor4(a[u], b[u]));
+      else {
+        st<NTS>(dst0 + i + u * step, a[u]);
+        st<NTS>(dst1 + i + u * step, b[u]);
+      }
+    }
+  }
+  for (; i < end; i += step) {
+    if constexpr (kPair) {
+      const uint4 a = ld<NTL>(src + 2 * i), b = ld<NTL>(src + 2 * i + 1);
+      if constexpr (MIX == FP8PROBE_HALF) {
+        st<NTS>(dst0 + i, xor4(a, b));
+      } else {
+        st<NTS>(dst0 + i, a);
+        st<NTS>(dst1 + i, b);
+      }
+    } else {
+      const uint4 a = ld<NTL>(src + i);
+      if constexpr (MIX == FP8PROBE_READ) acc = xor4(acc, a);
+      else st<NTS>(dst0 + i, a);
+    }
+  }
+  if constexpr (MIX == FP8PROBE_READ) {
+    if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0xF39CC060u && acc.w == 0x5CEDC834u) dst0[0] = acc;
   }
 }
 
 __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(int iters, uint64_t* clocks, float* sink) {
+  __shared__ float pad[kMfmaLdsWords];  // holds the compute unit: one workgroup each
   v8i a, b;  // E4M3 codes of 1.0 and 0.5, perturbed per lane
   const int t = threadIdx.x;
 #pragma unroll
@@ -100,7 +133,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(int iters, uint64
   float s = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMfmaAcc; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
-  if (s == 1234.5678f) sink[0] = s;
+  pad[t] = s;
+  __syncthreads();
+  if (pad[(t + 1) % (64 * kMfmaWaves)] == 1234.5678f) sink[0] = s;
   if (t == 0) {
     clocks[4 * blockIdx.x + 0] = c0;
     clocks[4 * blockIdx.x + 1] = c1;
@@ -130,25 +165,38 @@ int launched() { return hipGetLastError() == hipSuccess ? 0 : -6; }
 extern "C" {
 
 int fp8probe_stream(const void* src, int64_t n16, void* dst0, void* dst1, int mix, void* stream) {
-  if (mix < FP8PROBE_READ || mix > FP8PROBE_SPLIT) return -2;
-  if (n16 < 0 || ((mix == FP8PROBE_HALF || mix == FP8PROBE_SPLIT) && (n16 & 1))) return -3;
-  if (!src || !dst0 || (mix == FP8PROBE_SPLIT && !dst1)) return -1;
+  if ((mix & ~(15 | FP8PROBE_NT_LOAD | FP8PROBE_NT_STORE | FP8PROBE_BLOCKED)) || (mix & 15) > FP8PROBE_SPLIT) return -2;
+  const int base = mix & 15;
+  if (n16 < 0 || ((base == FP8PROBE_HALF || base == FP8PROBE_SPLIT) && (n16 & 1))) return -3;
+  if (!src || !dst0 || (base == FP8PROBE_SPLIT && !dst1)) return -1;
   if (((uintptr_t)src | (uintptr_t)dst0 | (uintptr_t)dst1) & 15u) return -5;
   if (n16 == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  const int64_t work = (mix == FP8PROBE_HALF || mix == FP8PROBE_SPLIT) ? n16 / 2 : n16;
+  const int64_t work = (base == FP8PROBE_HALF || base == FP8PROBE_SPLIT) ? n16 / 2 : n16;
   int64_t blocks = (int64_t)device_cus(st) * 8;
   const int64_t need = (work + kStreamThreads - 1) / kStreamThreads;
   blocks = blocks < need ? blocks : need;
   const uint4* s = reinterpret_cast<const uint4*>(src);
   uint4* d0 = reinterpret_cast<uint4*>(dst0);
   uint4* d1 = reinterpret_cast<uint4*>(dst1);
-  switch (mix) {
-    case FP8PROBE_READ: stream_kernel<FP8PROBE_READ><<<(unsigned)blocks, kStreamThreads, 0, st>>>(s, n16, d0, d1); break;
-    case FP8PROBE_COPY: stream_kernel<FP8PROBE_COPY><<<(unsigned)blocks, kStreamThreads, 0, st>>>(s, n16, d0, d1); break;
-    case FP8PROBE_HALF: stream_kernel<FP8PROBE_HALF><<<(unsigned)blocks, kStreamThreads, 0, st>>>(s, n16, d0, d1); break;
-    default: stream_kernel<FP8PROBE_SPLIT><<<(unsigned)blocks, kStreamThreads, 0, st>>>(s, n16, d0, d1); break;
+  const bool ntl = (mix & FP8PROBE_NT_LOAD) != 0, nts = (mix & FP8PROBE_NT_STORE) != 0;
+  const bool blk = (mix & FP8PROBE_BLOCKED) != 0;
+  auto go = [&](auto k) { k<<<(unsigned)blocks, kStreamThreads, 0, st>>>(s, n16, d0, d1); };
+#define FP8PROBE_LAUNCH2(M, B)                                    \
+  if (ntl && nts) go(stream_kernel<M, true, true, B>);            \
+  else if (ntl) go(stream_kernel<M, true, false, B>);             \
+  else if (nts) go(stream_kernel<M, false, true, B>);             \
+  else go(stream_kernel<M, false, false, B>);
+#define FP8PROBE_LAUNCH(M) \
+  if (blk) { FP8PROBE_LAUNCH2(M, true) } else { FP8PROBE_LAUNCH2(M, false) }
+  switch (base) {
+    case FP8PROBE_READ: FP8PROBE_LAUNCH(FP8PROBE_READ) break;
+    case FP8PROBE_COPY: FP8PROBE_LAUNCH(FP8PROBE_COPY) break;
+    case FP8PROBE_HALF: FP8PROBE_LAUNCH(FP8PROBE_HALF) break;
+    default: FP8PROBE_LAUNCH(FP8PROBE_SPLIT) break;
   }
+#undef FP8PROBE_LAUNCH2
+#undef FP8PROBE_LAUNCH
   return launched();
 }
 

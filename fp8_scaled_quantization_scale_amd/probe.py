@@ -13,6 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8mi_probe.so")
 
 READ, COPY, HALF, SPLIT = 0, 1, 2, 3
+NT_LOAD, NT_STORE, BLOCKED = 16, 32, 64  # access hints, OR-ed into a mix
 EXPORTS = ("fp8probe_stream", "fp8probe_mfma", "fp8probe_wall_clock_khz")
 MFMA_WAVES = 8                  # waves per workgroup of fp8probe_mfma
 MFMA_FLOPS_PER_ROUND = 8 * 2 * 16 * 16 * 128  # eight 16x16x128 products per wave per round
@@ -44,13 +45,15 @@ def _stream():
 
 def stream(src: torch.Tensor, dst0: torch.Tensor, dst1: torch.Tensor | None, mix: int) -> None:
     """One pass of fp8probe_stream over all of src (contiguous device tensors;
-    dst sizes as the header states: checked here)."""
+    dst sizes as the header states: checked here).  mix may carry NT_LOAD,
+    NT_STORE and BLOCKED."""
     n16 = src.numel() * src.element_size() // 16
-    out = n16 if mix == COPY else (n16 // 2 if mix in (HALF, SPLIT) else 1)
-    for t in (src, dst0) + ((dst1,) if mix == SPLIT else ()):
+    base = mix & 15
+    out = n16 if base == COPY else (n16 // 2 if base in (HALF, SPLIT) else 1)
+    for t in (src, dst0) + ((dst1,) if base == SPLIT else ()):
         if not (t.is_cuda and t.is_contiguous()):
             raise RuntimeError("probe buffers must be contiguous device tensors")
-    if dst0.numel() * dst0.element_size() < 16 * out or (mix == SPLIT and dst1.numel() * dst1.element_size() < 16 * out):
+    if dst0.numel() * dst0.element_size() < 16 * out or (base == SPLIT and dst1.numel() * dst1.element_size() < 16 * out):
         raise RuntimeError("probe output buffer too small")
     st = load().fp8probe_stream(src.data_ptr(), n16, dst0.data_ptr(), None if dst1 is None else dst1.data_ptr(),
                                 mix, _stream())

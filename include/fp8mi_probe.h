@@ -29,21 +29,30 @@ extern "C" {
                          /* (a BF16 -> FP8 cast writing one code layout)          */
 #define FP8PROBE_SPLIT 3 /* dst0[i] = src[2i], dst1[i] = src[2i+1]: 2 in, 1+1 out */
                          /* (a cast writing both code layouts)                   */
+/* access hints, OR-ed into `mix` */
+#define FP8PROBE_NT_LOAD 16  /* non-temporal loads (the data is read once)    */
+#define FP8PROBE_NT_STORE 32 /* non-temporal stores                           */
+#define FP8PROBE_BLOCKED 64  /* each workgroup streams one contiguous range  */
+                             /* (default: grid-strided)                       */
 
 /* fp8probe_stream -- one streaming pass over n16 16-byte chunks of src
- * (16-byte aligned), grid-strided over every compute unit with four loads
- * in flight per thread.  dst0 (and dst1 for SPLIT) receive n16 (COPY) or
+ * (16-byte aligned) by eight workgroups per compute unit, eight 16-byte
+ * loads in flight per thread, grid-strided or (FP8PROBE_BLOCKED) in one
+ * contiguous range per workgroup.  dst0 (and dst1 for SPLIT) receive n16 (COPY) or
  * n16 / 2 (HALF, SPLIT) chunks; READ stores at most one 16-byte chunk into
  * dst0 (only when the XOR of the data is a fixed sentinel, which keeps the
  * reads live), so dst0 must hold 16 bytes.  HALF and SPLIT need n16 even.
  * Returns FP8MI_OK, -1 (NULL pointer), -2 (bad mix), -3 (n16 < 0 or odd
- * where it must be even), -5 (misaligned) or -6 (launch failed). */
+ * where it must be even), -5 (misaligned) or -6 (launch failed).  `mix` is
+ * one of the mixes above, optionally OR-ed with any of FP8PROBE_NT_LOAD,
+ * FP8PROBE_NT_STORE and FP8PROBE_BLOCKED. */
 int fp8probe_stream(const void* src, int64_t n16, void* dst0, void* dst1, int mix, void* stream);
 
 /* fp8probe_mfma -- `iters` rounds of eight independent 16x16x128 FP8
  * matrix-core products (v_mfma_f32_16x16x128_f8f6f4, E4M3 operands held in
  * registers, no memory traffic) on every SIMD: two waves per SIMD, one
- * workgroup of eight waves per compute unit, `workgroups` of them.  Flops
+ * workgroup of eight waves per compute unit (each holds 96 KB of LDS, so no
+ * second one fits), `workgroups` of them.  Flops
  * = workgroups * 8 waves * iters * 8 * 65536.  clocks [4 * workgroups]
  * receives per workgroup the core cycle counter and the constant-rate wall
  * counter at the start and the end of its loop (c0, c1, w0, w1), so the

@@ -199,7 +199,8 @@ def test_probe_library_exports_every_declared_symbol():
     assert set(declared) <= set(re.findall(r" T (fp8probe_\w+)$", out, flags=re.M))
     defs = dict(re.findall(r"^#define FP8PROBE_(\w+) (\d+)", open(PROBE_HEADER).read(), flags=re.M))
     assert {k: int(v) for k, v in defs.items()} == {"READ": probe.READ, "COPY": probe.COPY, "HALF": probe.HALF,
-                                                     "SPLIT": probe.SPLIT}
+                                                     "SPLIT": probe.SPLIT, "NT_LOAD": probe.NT_LOAD,
+                                                     "NT_STORE": probe.NT_STORE, "BLOCKED": probe.BLOCKED}
 
 
 def test_probe_validation():
@@ -207,6 +208,9 @@ def test_probe_validation():
 
     lib = probe.load()
     assert lib.fp8probe_stream(GOOD, 64, GOOD, None, 9, None) == -2
+    assert lib.fp8probe_stream(GOOD, 64, GOOD, None, probe.COPY | 128, None) == -2  # unknown hint bit
+    assert lib.fp8probe_stream(GOOD, 63, GOOD, GOOD, probe.HALF | probe.NT_LOAD, None) == -3  # hints keep the checks
+    assert lib.fp8probe_stream(GOOD, 0, GOOD, None, probe.COPY | probe.NT_LOAD | probe.NT_STORE, None) == 0
     assert lib.fp8probe_stream(GOOD, 63, GOOD, GOOD, probe.HALF, None) == -3
     assert lib.fp8probe_stream(GOOD, -1, GOOD, None, probe.COPY, None) == -3
     assert lib.fp8probe_stream(None, 64, GOOD, None, probe.COPY, None) == -1

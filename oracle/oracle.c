@@ -360,8 +360,13 @@ int or_history_update(float* ring, int32_t* head, int len, float amax, int fmt, 
 {
     int pushed = 0;
     if (isfinite(amax)) {
-        ring[*head] = amax;
-        *head = (*head + 1) % len;
+        /* a stored head outside [0, len) (state saved with another length)
+           is taken modulo len, the reading the C ABI documents */
+        int h = *head % len;
+        if (h < 0)
+            h += len;
+        ring[h] = amax;
+        *head = (h + 1) % len;
         pushed = 1;
     } else {
         *nonfinite += 1;

@@ -306,3 +306,23 @@ def test_history_skips_nonfinite_and_restores():
         c.update(v)
     assert np.array_equal(a.ring, c.ring) and a.head[0] == c.head[0]
     assert a.scale == c.scale and a.scale_inv == c.scale_inv
+
+
+def test_history_head_outside_the_ring_is_taken_modulo_len():
+    # The pages fix a ring of the last N amaxes but not what a stored head
+    # outside [0, N) means (state saved with another length); the C ABI's
+    # reading, which the oracle follows, is head mod N.  Pinned by hand for
+    # N = 5: the amax lands in slot (head mod 5) and the head moves one on.
+    for head, slot in ((7, 2), (-1, 4), (12, 2), (5, 0), (-6, 4)):
+        h = oracle.History("e4m3", 5)
+        h.head[0] = head
+        h.update(np.float32(3.0))
+        want = np.zeros(5, np.float32)
+        want[slot] = 3.0
+        assert np.array_equal(h.ring, want), head
+        assert h.head[0] == (slot + 1) % 5, head
+    # a non-finite amax pushes nothing and leaves the stored head as it was
+    h = oracle.History("e4m3", 5)
+    h.head[0] = 7
+    h.update(np.float32(np.nan))
+    assert h.head[0] == 7 and not h.ring.any() and h.nonfinite[0] == 1

@@ -21,6 +21,14 @@ int hip_status(hipError_t e) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// rows x ld elements of esize bytes span a byte range that fits in int64 (no
+// array that large can exist; checking first keeps every later size
+// computation here and in the launchers free of overflow)
+bool extent_ok(int64_t rows, int64_t ld, int64_t esize) {
+  int64_t n = 0;
+  return !__builtin_mul_overflow(rows, ld, &n) && !__builtin_mul_overflow(n, esize, &n);
+}
+
 // the persistent GEMM grid numbers its 256 x 256 output tiles with 32-bit ints
 bool tile_count_ok(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256) <= 0x7FFFFFFFLL; }
 
@@ -49,6 +57,9 @@ int check_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
   if (row && ld_q_row < cols) return FP8MI_ERR_SHAPE;
   if (col && ld_q_col < rows) return FP8MI_ERR_SHAPE;
   const int64_t esize = x_dtype == FP8MI_IN_BF16 ? 2 : 4;
+  if (!extent_ok(rows, ld_x, esize)) return FP8MI_ERR_SHAPE;
+  if (row && !extent_ok(rows, ld_q_row, 1)) return FP8MI_ERR_SHAPE;
+  if (col && !extent_ok(cols, ld_q_col, 1)) return FP8MI_ERR_SHAPE;
   if (!aligned16(x) || (ld_x * esize) % 16) return FP8MI_ERR_ALIGN;
   if (row && (!aligned16(q_row) || ld_q_row % 16)) return FP8MI_ERR_ALIGN;
   if (col && (!aligned16(q_col) || ld_q_col % 16)) return FP8MI_ERR_ALIGN;
@@ -70,6 +81,7 @@ int check_gemm(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda, const 
   if (M == 0 || N == 0) return FP8MI_OK;
   if (!c) return FP8MI_ERR_NULL;
   if (ldc < N) return FP8MI_ERR_SHAPE;
+  if (!extent_ok(M, ldc, c_dtype == FP8MI_OUT_FP32 ? 4 : 2)) return FP8MI_ERR_SHAPE;
   if (K > 0) {
     if (!a || !b || !s_a || !s_b) return FP8MI_ERR_NULL;
     if (K % 16) return FP8MI_ERR_SHAPE;
@@ -143,6 +155,7 @@ int fp8_bf16_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_
   if (M == 0 || N == 0) return FP8MI_OK;
   if (!c) return FP8MI_ERR_NULL;
   if (ldc < N) return FP8MI_ERR_SHAPE;
+  if (!extent_ok(M, ldc, c_dtype == FP8MI_OUT_FP32 ? 4 : 2)) return FP8MI_ERR_SHAPE;
   if (K > 0) {
     if (!a || !b) return FP8MI_ERR_NULL;
     if (K % 8) return FP8MI_ERR_SHAPE;

@@ -167,9 +167,10 @@ extern "C" {
  *        channel and block recipes; those blocks use s = 1, MX byte 0xFF).
  * x must not overlap any output.
  * Alignment: x, q_row, q_col 16-byte aligned; ld_x * sizeof(elem),
- * ld_q_row and ld_q_col multiples of 16 bytes.  Sizes: CHANNEL needs
- * ceil(rows/128) * ceil(cols/128) < 2^31 (else FP8MI_ERR_UNSUPPORTED); the
- * other recipes take any size.  rows == 0 or cols == 0 is
+ * ld_q_row and ld_q_col multiples of 16 bytes.  Sizes: rows * ld_x *
+ * sizeof(elem), rows * ld_q_row and cols * ld_q_col must fit in int64 (else
+ * FP8MI_ERR_SHAPE); CHANNEL needs ceil(rows/128) * ceil(cols/128) < 2^31
+ * (else FP8MI_ERR_UNSUPPORTED); the other recipes take any size.  rows == 0 or cols == 0 is
  * allowed (CURRENT then writes amax = 0, scale = scale_inv = 1).
  * Returns FP8MI_OK or an FP8MI_ERR_* code; nothing is launched on error. */
 int fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
@@ -245,7 +246,8 @@ int fp8_amax_history_update(float* history, int32_t* head, int64_t len, float* a
  * s_a, s_b 4-byte aligned (scale grids are read in aligned dwords; for MX
  * that may touch up to 3 bytes past a grid's last row, never used),
  * lda, ldb multiples of 16, K <= lda, ldb <= 4194304 and
- * ceil(M/256) * ceil(N/256) < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N.
+ * ceil(M/256) * ceil(N/256) < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N
+ * with M * ldc * sizeof(c element) fitting in int64 (else FP8MI_ERR_SHAPE).
  * c must not overlap a, b or the scales.  K == 0 writes zeros.
  * Tolerance vs a float64 reference over the dequantized operands:
  * |C - C_ref| <= 2^-10 sum_k |a b| (+ 2^-8 |C_ref| for BF16 output). */
@@ -264,7 +266,8 @@ int fp8_gemm_scaled(const uint8_t* a, int fmt_a, const void* s_a, int64_t lda,
  *   c [M x N] (c_dtype), ldc.  C[i][j] = sum_k a[i][k] * b[j][k].
  * Requirements: M, N, K >= 0; K % 8 == 0; a, b 16-byte aligned, lda, ldb
  * multiples of 8, K <= lda, ldb <= 2097152 and ceil(M/256) * ceil(N/256)
- * < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N.  K == 0 writes zeros.  Errors as for fp8_gemm_scaled.
+ * < 2^31 (else FP8MI_ERR_UNSUPPORTED); ldc >= N, M * ldc * sizeof(c element)
+ * fitting in int64.  K == 0 writes zeros.  Errors as for fp8_gemm_scaled.
  * Tolerance vs a float64 reference: as fp8_gemm_scaled. */
 int fp8_bf16_gemm(const void* a, int64_t lda, const void* b, int64_t ldb,
                   int64_t M, int64_t N, int64_t K,

@@ -49,8 +49,10 @@
 //               four products behind the matrix core; the last row's
 //               promotions of a step run at the start of the wave's next
 //               load phase, off the matrix core's critical path.
-// Per-step scale words travel like the tiles: 4-byte-per-lane LDS DMA into a
-// small staging area next to each stage.
+// Scale words travel like the tiles, by LDS DMA, but four K steps at a time:
+// one 16-byte request per operand row brings the row's scales of four steps
+// (a per-step dword would cost the texture path one cache-line request per
+// row per step), into two small group buffers beside the tile stages.
 //
 // The same kernel, with BF16 operands and v_mfma_f32_16x16x32_bf16, is the
 // BF16 GEMM FP8's speedup is measured against ("Mastering FP8 LLM training",
@@ -93,12 +95,13 @@ constexpr int kLag = 4;                  // promotion distance behind the MFMAs
 constexpr int kAhead = 1;                // A sub-tiles read ahead of the MFMAs
 constexpr int kRingA = kAhead + 1;       // A fragments held
 constexpr int kRingS = kAhead + 2;       // A row scales held (a row's promotions trail one row)
-// per-stage scale staging: A rows in eight 256-byte slots, slot r / 32 holding
-// row r's word at 4 (r % 32) and (MX) the dword after it 128 bytes further on;
-// then B row words, then the dword after each (MX rows whose E8M0 bytes
-// straddle a dword)
-constexpr int kSclA = 0, kSclB = 2048, kSclBHi = 3072, kSclBytes = 4096;
-__device__ __forceinline__ int a_scl_off(int row) { return kSclA + (row >> 5) * 256 + 4 * (row & 31); }
+// Scales travel in groups of kSG K steps, two group buffers: each operand
+// row's FP32 words (or E8M0 bytes) for the group as 16 bytes at LO + 16 row,
+// taken from the aligned dword holding the first; an MX row whose bytes run
+// past those 16 takes the dword after them from HI + 4 row.  A 128-row tile
+// scale takes 16 bytes per tile at LO + 1024 t (A) or LO + 16 t (B).
+constexpr int kSG = 4;
+constexpr int kSclALo = 0, kSclAHi = 4096, kSclBLo = 5120, kSclBHi = 9216, kSclBytes = 10240;
 
 template <int FA, int FB>
 __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
@@ -181,16 +184,13 @@ struct Scl {
   static constexpr bool kTileB = REC == kGemmBlock128x128 || REC == kGemmBlock2d;     // FP32 per 128-row B tile
   static constexpr bool kMx = REC == kGemmMx;
   static constexpr bool kPromote = kRowA || kTileA;
-  // scale DMAs per wave per step: A by the group that owns the rows (MX low
-  // and next dword in one), B by group 0 (MX: low and next dword)
-  static constexpr int kNsA = (kMx || kRowA || kTileA) ? 1 : 0;
-  static constexpr int kNsB = kMx ? 2 : ((kRowB || kTileB) ? 1 : 0);
+  static constexpr bool kSclAny = kRowA || kTileA || kRowB || kTileB || kMx;
 };
 
 template <int FA, int FB, int REC, int OUT>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
   using S = Scl<REC>;
-  constexpr bool kScl = S::kNsA + S::kNsB > 0;
+  constexpr bool kScl = S::kSclAny;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sscl[2][kScl ? kSclBytes : 16];
 
@@ -274,51 +274,51 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
       asm volatile("" : "+s"(lb));
       dma16(rs, lb + seg * 1024, vo, (uint32_t)k0);
     };
-    // Scale words of step kt.  A side: wave q of group g brings rows
-    // 128 g + 32 q + (l % 32), lanes l >= 32 the dword after (MX; else
-    // nothing); for a 128-row tile scale lane 0 of wave 0 brings tile g's
-    // word.  B side (group 0): rows 64 q + l, `hi` the dword after (MX); for
-    // tile scales lanes 0 and 1 of wave 0 bring the two tiles' words.
-    auto dma_scl = [&](bool hi, int kt, bool a_side, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
-      uint32_t vo;
-      int off;
+    // Scales of the kSG steps from kt on (kt a multiple of kSG) into group
+    // buffer (kt / kSG) & 1.  A side, each group its own 128 rows: waves
+    // q = 0, 1 bring rows 128 g + 64 q + l (16 bytes each), MX waves q = 2, 3
+    // the dwords after them; a 128-row tile scale comes from lane 0 of wave
+    // 0.  B side, group 0: wave q brings rows 64 q + l (MX: and the dwords
+    // after them), or lanes 0 and 1 of wave 0 the two tiles' words.  Lanes
+    // with nothing to bring read past the range (zeros) into slack space.
+    auto dma_scl = [&](int kt, bool a_side, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+      uint32_t sb = __builtin_amdgcn_readfirstlane(scl_base + ((kt / kSG) & 1) * kSclBytes);
+      asm volatile("" : "+s"(sb));
+      auto first = [&](int row) -> uint32_t {  // aligned start of a row's group window
+        return S::kMx ? ((((uint32_t)(row * p.nkb)) & ~3u) + 4u * kt) : (uint32_t)((row * p.nkb + kt) * 4);
+      };
       if (a_side) {
         if constexpr (S::kTileA) {
-          vo = (q == 0 && lane == 0) ? (uint32_t)((grp * p.nkb + kt) * 4) : kOOB;
-        } else if constexpr (S::kMx) {
-          const int row = 128 * grp + 32 * q + (lane & 31);
-          vo = (((uint32_t)(row * p.nkb)) & ~3u) + 4u * kt + (lane >= 32 ? 4u : 0u);
+          if (q == 0) dma16(rs, sb + kSclALo + 1024 * grp, lane == 0 ? (uint32_t)((grp * p.nkb + kt) * 4) : kOOB, 0);
         } else {
-          vo = lane < 32 ? (uint32_t)(((128 * grp + 32 * q + lane) * p.nkb + kt) * 4) : kOOB;
+          if (q < 2) dma16(rs, sb + kSclALo + 16 * (128 * grp + 64 * q), first(128 * grp + 64 * q + lane), 0);
+          if constexpr (S::kMx)
+            if (q >= 2) dma4(rs, sb + kSclAHi + 4 * (128 * grp + 64 * (q - 2)), first(128 * grp + 64 * (q - 2) + lane) + 16u);
         }
-        off = kSclA + (4 * grp + q) * 256;
       } else {
         if constexpr (S::kTileB) {
-          vo = (q == 0 && lane < 2) ? (uint32_t)((lane * p.nkb + kt) * 4) : kOOB;
-        } else if constexpr (S::kMx) {
-          const int row = 64 * q + lane;
-          vo = (((uint32_t)(row * p.nkb)) & ~3u) + 4u * kt + (hi ? 4u : 0u);
+          if (q == 0) dma16(rs, sb + kSclBLo, lane < 2 ? (uint32_t)((lane * p.nkb + kt) * 4) : kOOB, 0);
         } else {
-          vo = (uint32_t)(((64 * q + lane) * p.nkb + kt) * 4);
+          dma16(rs, sb + kSclBLo + 16 * 64 * q, first(64 * q + lane), 0);
+          if constexpr (S::kMx) dma4(rs, sb + kSclBHi + 4 * 64 * q, first(64 * q + lane) + 16u);
         }
-        off = (hi ? kSclBHi : kSclB) + q * 256;
       }
-      uint32_t sb = __builtin_amdgcn_readfirstlane(scl_base + (kt & 1) * kSclBytes);
-      asm volatile("" : "+s"(sb));
-      dma4(rs, sb + off, vo);
     };
     // This wave's DMA set for step kt.  Each group moves its own 128 A rows
     // (wave q: segments 4 q.. of its half) and their scales; group 0 also
-    // the whole B tile (wave q: segments 32 + 8 q..) and B scales.
+    // the whole B tile (wave q: segments 32 + 8 q..) and B scales.  Scales
+    // go out with the first step of each group of kSG.
     auto issue_set = [&](int kt, auto Tail) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_tile(16 * grp + 4 * q + i, kt, true, ra, p.lda, Tail);
-      if constexpr (S::kNsA > 0) dma_scl(false, kt, true, rsa);
+      const bool scl = (kt % kSG) == 0;
+      if constexpr (S::kRowA || S::kTileA || S::kMx)
+        if (scl) dma_scl(kt, true, rsa);
       if (grp == 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) dma_tile(32 + 8 * q + i, kt, false, rb, p.ldb, Tail);
-#pragma unroll
-        for (int h = 0; h < S::kNsB; ++h) dma_scl(h == 1, kt, false, rsb);
+        if constexpr (S::kRowB || S::kTileB || S::kMx)
+          if (scl) dma_scl(kt, false, rsb);
       }
     };
     auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -367,9 +367,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     // multiples of 4 rows), so byte mis + lg sits at a fixed per-lane offset
     // from the row's low word: in that word, or in the dword after it (A: 128
     // bytes further on in the row's slot, B: in the high array).
-    auto mx_off = [&](bool a_side) __attribute__((always_inline)) -> int {
-      const int b = (((lr & 3) * p.nkb) & 3) + lg;
-      return b < 4 ? b : (a_side ? 128 : kSclBHi - kSclB) + b - 4;
+    // group window byte of this lane's block of step kt: b = mis + lg + 4 (kt % kSG)
+    auto mx_b = [&](int kt) __attribute__((always_inline)) -> int {
+      return (((lr & 3) * p.nkb) & 3) + lg + 4 * (kt % kSG);
+    };
+    // where row `row`'s byte b sits: in its 16 bytes at LO, or in the dword after at HI
+    auto mx_at = [&](const uint8_t* sc, int lo, int hi, int row, int b) __attribute__((always_inline)) -> const uint8_t* {
+      return b < 16 ? sc + lo + 16 * row + b : sc + hi + 4 * row + (b - 16);
     };
     // E8M0 byte of a row (in the last step, blocks past K are masked at the
     // start of the multiply phase)
@@ -397,10 +401,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     // A sub-tile i of step kt (rows 16 i.. of the group's half) and its row scale
     auto load_a = [&](int kt, int i) __attribute__((always_inline)) {  // i is a constant at every (inlined) call
       const uint8_t* la = smem + (kt & 1) * kTileBytes;
-      const uint8_t* sc = &sscl[kt & 1][0];
+      const uint8_t* sc = &sscl[(kt / kSG) & 1][0];
       const int row = wm * kWM + i * 16 + lr;
       fa[i % kRingA] = frag(la, row, swz_a(row));
-      if constexpr (S::kRowA) bsa[i % kRingS] = *reinterpret_cast<const float*>(sc + a_scl_off(row));
+      if constexpr (S::kRowA)
+        bsa[i % kRingS] = *reinterpret_cast<const float*>(sc + kSclALo + 16 * row + 4 * (kt % kSG));
     };
 
     // ---- load phase of step kt: B fragments and B-side scales into
@@ -412,23 +417,24 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
         const int row = wn * kWN + brow(j);
         fb[j] = frag(lb, row, swz_b(row));
       }
-      const uint8_t* sc = &sscl[kt & 1][0];
+      const uint8_t* sc = &sscl[(kt / kSG) & 1][0];
+      const int ks = 4 * (kt % kSG);  // the step's word in a row's 16 bytes
       if constexpr (S::kRowB) {
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const float4 w = *reinterpret_cast<const float4*>(sc + kSclB + 4 * (wn * kWN + lg * kCPL + 4 * j));
-          bsb[j][0] = w.x; bsb[j][1] = w.y; bsb[j][2] = w.z; bsb[j][3] = w.w;
-        }
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bsb[j][e] = *reinterpret_cast<const float*>(sc + kSclBLo + 16 * (wn * kWN + lg * kCPL + 4 * j + e) + ks);
       }
-      if constexpr (S::kTileB) stile = *reinterpret_cast<const float*>(sc + kSclB + 4 * (wn / 2));
+      if constexpr (S::kTileB) stile = *reinterpret_cast<const float*>(sc + kSclBLo + 16 * (wn / 2) + ks);
       // this group's own A rows (landed by its own waits): the 2-D recipe's
       // A tile scale, the MX row bytes, and the first sub-tile, so that the
       // multiply phase opens with MFMAs
-      if constexpr (S::kTileA) stile *= *reinterpret_cast<const float*>(sc + kSclA + wm * 1024);
+      if constexpr (S::kTileA) stile *= *reinterpret_cast<const float*>(sc + kSclALo + 1024 * wm + ks);
       if constexpr (S::kMx) {
-        const uint8_t* at = sc + a_scl_off(wm * kWM + lr) + mx_off(true);
+        const int b = mx_b(kt);
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) sax[i] = mx_byte(at + (i >> 1) * 256 + (i & 1) * 64);
+        for (int i = 0; i < kMT; ++i) sax[i] = mx_byte(mx_at(sc, kSclALo, kSclAHi, wm * kWM + i * 16 + lr, b));
       }
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) load_a(kt, i);
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
           const int r = wn * kWN + brow(j);
-          sbx[j] = mx_byte(sc + kSclB + 4 * r + mx_off(false));
+          sbx[j] = mx_byte(mx_at(sc, kSclBLo, kSclBHi, r, mx_b(kt)));
         }
       }
     };

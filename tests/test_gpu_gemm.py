@@ -80,6 +80,25 @@ def test_gemm_matches_reference(recipe, fa, fb, out):
         _check(c, da, db, name)
 
 
+# K steps of 128 bytes that fill several four-step scale groups and end in a
+# partial one (KT = 10 and 14), MX rows whose E8M0 bytes start mid-dword
+# (ceil(K / 32) = 37 and 53 bytes per row), ragged tile edges in M and N, and
+# (4352 x 4352: 289 output tiles) more tiles than workgroups, so that
+# workgroups carry their scale and stage state from one tile to the next.
+WALK_SHAPES = [(4352, 4352, 1168), (300, 700, 1680)]
+
+
+@pytest.mark.parametrize("recipe", RECIPES)
+def test_gemm_scale_groups_and_tile_walk(recipe):
+    need_gpu()
+    for i, (M, N, K) in enumerate(WALK_SHAPES):
+        fa, fb, out = (fm.E4M3, fm.E4M3, fm.OUT_BF16) if i == 0 else (fm.E5M2, fm.E4M3, fm.OUT_FP32)
+        name, dt = OUT[out]
+        a, sa, da, b, sb, db = _operands(recipe, M, N, K, fa, fb, 2000 + 10 * i)
+        c = fm.gemm(a, fa, sa, b, fb, sb, recipe, K, dt, M=M, N=N)
+        _check(c, da, db, name)
+
+
 def test_tiny_blockwise_config_in_full():
     """The tiny blockwise workload: A 128 x 512 (1% outlier columns x50) in
     1x128 tiles, B 512 x 256 N(0, 0.02) in 128 x 128 tiles, BF16 out."""

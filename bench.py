@@ -316,7 +316,7 @@ def _threads() -> int:
     return len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
 
 
-def cpu_baseline(cfg: workloads.Config, rows: int = 512, out_rows: int = 512):
+def cpu_baseline(cfg: workloads.Config, rows: int = 1024, out_rows: int = 768):
     """Time the oracle on a bounded sample of the step and extrapolate to the
     full step.  Quantize: `rows` whole rows of X, G and W (their codes and
     scales in every layout the step writes), cost scaled by M / rows (X, G)

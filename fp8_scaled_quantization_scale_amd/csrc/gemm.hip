@@ -361,13 +361,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     // B row (tile row within the wave's 64) that lane row lr loads for sub-tile j:
     // lane group g' = lr / 4 of the C^T result covers columns [g' CPL, (g'+1) CPL)
     auto brow = [&](int j) __attribute__((always_inline)) { return (lr >> 2) * kCPL + 4 * j + (lr & 3); };
-    // MX: lane group lg feeds K block 4 kt + lg of its row.  A row's 4 step
-    // bytes start mis = (row nkb) % 4 bytes into its staged dword pair; mis
-    // is ((lr % 4) nkb) % 4 for every row a lane reads (tiles start on
-    // multiples of 4 rows), so byte mis + lg sits at a fixed per-lane offset
-    // from the row's low word: in that word, or in the dword after it (A: 128
-    // bytes further on in the row's slot, B: in the high array).
-    // group window byte of this lane's block of step kt: b = mis + lg + 4 (kt % kSG)
+    // MX: lane group lg feeds K block 4 kt + lg of its row.  A row's bytes
+    // for a scale group start mis = (row nkb) % 4 bytes into its staged
+    // window (16 bytes from the aligned dword holding the first, then the
+    // dword after them); mis is ((lr % 4) nkb) % 4 for every row a lane reads
+    // (tiles start on multiples of 4 rows), so the lane's byte of step kt is
+    // window byte b = mis + lg + 4 (kt % kSG), the same for all its rows.
     auto mx_b = [&](int kt) __attribute__((always_inline)) -> int {
       return (((lr & 3) * p.nkb) & 3) + lg + 4 * (kt % kSG);
     };
@@ -534,7 +533,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     // (and its scales) by its own group in L(k-1) and C(k-1), all in phases
     // before L0(k) / L1(k).  Each wave waits for its whole set at the end of
     // C(k), so the barrier there publishes group 0's B for L0(k+1) and every
-    // group's A half for its own L(k+1).
+    // group's A half for its own L(k+1).  Scales go out with the first step
+    // of each group of kSG into the group buffer last used kSG to 2 kSG - 1
+    // steps before, whose last reads are long done.
     if (grp == 1) __syncthreads();
 #pragma unroll 1
     for (int k = 0; k < KT; ++k) {

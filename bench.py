@@ -691,7 +691,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.CONFIGS))
-    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies the steps rotate over (0: at least 4, and enough that every "
+                         "input's copies exceed 512 MiB, twice the Infinity Cache)")
     ap.add_argument("--event-every", type=int, default=2, metavar="E",
                     help="bracket the dominant and fprop GEMMs with timing events in every E-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -723,6 +725,9 @@ def main():
         print(json.dumps(latency_line(cfg, args, ev)))
         return
 
+    if args.rotate <= 0:
+        smallest = min(t.rows * t.cols * 2 for t in (cfg.X, cfg.W, cfg.G))  # BF16 bytes
+        args.rotate = max(4, -(-(512 << 20) // smallest) + 1)
     step = Step(cfg, args.rotate)
     torch.cuda.synchronize()
     for i in range(args.warmup):

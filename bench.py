@@ -464,13 +464,14 @@ def _cpu_model() -> str:
 # ---------------------------------------------------------------------------
 
 def _source_sha() -> str:
-    """Hash of the sources that define the kernels and their launch
-    configuration (the HIP files and the two internal headers; the C ABI's
-    host-side validation in api.cpp does not change what a kernel moves)."""
+    """Hash of the sources that define the path's kernels and their launch
+    configuration (the HIP files and the two internal headers; not the C
+    ABI's host-side validation in api.cpp, which does not change what a
+    kernel moves, nor the measurement kernels of probe.hip)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_scaled_quantization_scale_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith(".hip") or f in ("device.hpp", "launch.hpp"):
+        if (f.endswith(".hip") and f != "probe.hip") or f in ("device.hpp", "launch.hpp"):
             with open(os.path.join(csrc, f), "rb") as fh:
                 h.update(fh.read())
     return h.hexdigest()[:16]
@@ -662,6 +663,17 @@ def latency_line(cfg: workloads.Config, args, ev: "HipEvents") -> dict:
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     replay = _time_ms(graph.replay, reps, ev) * 1e3
+    # the floor: three launches of an empty kernel, eagerly and as a graph
+    empty3 = lambda: [probe.empty(1, 256) for _ in range(3)]  # noqa: E731
+    floor_eager = _time_ms(empty3, reps, ev) * 1e3
+    floor_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        empty3()
+        with torch.cuda.graph(floor_graph, stream=side):
+            empty3()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    floor_replay = _time_ms(floor_graph.replay, reps, ev) * 1e3
     return {
         "metric": "FP8 blockwise step latency (quantize A 1x128, quantize B 128x128, fprop GEMM)",
         "value": round(replay, 2), "unit": "us", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
@@ -669,6 +681,8 @@ def latency_line(cfg: workloads.Config, args, ev: "HipEvents") -> dict:
         "config": {"workload": cfg.name, "recipe": cfg.recipe, "M": M, "N": N, "K": K, "inputs": "bf16",
                    "outputs": "bf16"},
         "eager_us": round(eager, 2), "graph_replay_us": round(replay, 2), "kernels_us": per_op,
+        "launch_floor_us": {"eager": round(floor_eager, 2), "graph_replay": round(floor_replay, 2),
+                            "what": "three launches of an empty kernel (fp8probe_empty, one workgroup)"},
         "note": "latency-bound case: value is one replay of a HIP graph holding the three launches; eager_us the "
                 "same three launches issued from Python; median of 3 blocks of 200 back-to-back steps",
     }

@@ -144,6 +144,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(int iters, uint64
   }
 }
 
+// Does nothing: a dispatch of it costs what any launch of that shape costs.
+__global__ void empty_kernel() {}
+
 int stream_device(hipStream_t st) {
   int dev = -1;
   if (st == nullptr || hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0)
@@ -204,6 +207,12 @@ int fp8probe_mfma(int iters, int workgroups, uint64_t* clocks, float* sink, void
   if (iters < 1 || workgroups < 1) return -3;
   if (!clocks || !sink) return -1;
   mfma_kernel<<<(unsigned)workgroups, 64 * kMfmaWaves, 0, (hipStream_t)stream>>>(iters, clocks, sink);
+  return launched();
+}
+
+int fp8probe_empty(int workgroups, int threads, void* stream) {
+  if (workgroups < 1 || threads < 1 || threads > 1024) return -3;
+  empty_kernel<<<(unsigned)workgroups, (unsigned)threads, 0, (hipStream_t)stream>>>();
   return launched();
 }
 

@@ -1,7 +1,8 @@
 """Binding of libfp8mi_probe.so (include/fp8mi_probe.h): the measurement
 kernels bench.py uses to state what this GPU sustains -- the FP8 matrix-core
-rate and shader clock under full load, and HBM streams at the quantize
-kernels' read:write mixes.  Argument marshalling only."""
+rate and shader clock under full load, HBM streams at the quantize
+kernels' read:write mixes, and the cost of an empty launch.  Argument
+marshalling only."""
 from __future__ import annotations
 
 import ctypes
@@ -14,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8mi_probe.so")
 
 READ, COPY, HALF, SPLIT = 0, 1, 2, 3
 NT_LOAD, NT_STORE, BLOCKED = 16, 32, 64  # access hints, OR-ed into a mix
-EXPORTS = ("fp8probe_stream", "fp8probe_mfma", "fp8probe_wall_clock_khz")
+EXPORTS = ("fp8probe_stream", "fp8probe_mfma", "fp8probe_empty", "fp8probe_wall_clock_khz")
 MFMA_WAVES = 8                  # waves per workgroup of fp8probe_mfma
 MFMA_FLOPS_PER_ROUND = 8 * 2 * 16 * 16 * 128  # eight 16x16x128 products per wave per round
 
@@ -33,6 +34,8 @@ def load(path: str = LIB_PATH):
     lib.fp8probe_stream.argtypes = [vp, i64, vp, vp, i32, vp]
     lib.fp8probe_mfma.restype = i32
     lib.fp8probe_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.fp8probe_empty.restype = i32
+    lib.fp8probe_empty.argtypes = [i32, i32, vp]
     lib.fp8probe_wall_clock_khz.restype = i32
     lib.fp8probe_wall_clock_khz.argtypes = [vp]
     _lib = lib
@@ -68,6 +71,13 @@ def mfma(iters: int, workgroups: int, clocks: torch.Tensor, sink: torch.Tensor) 
     st = load().fp8probe_mfma(iters, workgroups, clocks.data_ptr(), sink.data_ptr(), _stream())
     if st != 0:
         raise RuntimeError(f"fp8probe_mfma failed ({st})")
+
+
+def empty(workgroups: int = 1, threads: int = 256) -> None:
+    """One launch of fp8probe_empty (a kernel that does nothing)."""
+    st = load().fp8probe_empty(workgroups, threads, _stream())
+    if st != 0:
+        raise RuntimeError(f"fp8probe_empty failed ({st})")
 
 
 def wall_clock_khz() -> int:

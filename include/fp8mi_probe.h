@@ -8,7 +8,8 @@
  * fraction of the theoretical rate it reaches.  The datasheet peaks assume
  * the top clock and ideal memory; these kernels measure the matrix-core
  * rate and shader clock under full FP8 MFMA load, and the HBM rate of plain
- * streams with the quantize kernels' read:write byte mixes.
+ * streams with the quantize kernels' read:write byte mixes, and the cost
+ * of an empty launch.
  *
  * Conventions as in fp8mi.h: device pointers, `stream` a hipStream_t, int
  * status (FP8MI_OK = 0 or a negative FP8MI_ERR_* code), nothing allocated.
@@ -61,6 +62,12 @@ int fp8probe_stream(const void* src, int64_t n16, void* dst0, void* dst1, int mi
  * written in practice (keeps the products live).
  * Returns FP8MI_OK, -1 (NULL pointer), -3 (iters or workgroups < 1) or -6. */
 int fp8probe_mfma(int iters, int workgroups, uint64_t* clocks, float* sink, void* stream);
+
+/* fp8probe_empty -- one launch of a kernel with an empty body, `workgroups`
+ * workgroups of `threads` threads: the cost of a dispatch alone, the floor
+ * under a launch-latency-bound step.  Returns FP8MI_OK, -3 (workgroups < 1,
+ * threads outside 1..1024) or -6. */
+int fp8probe_empty(int workgroups, int threads, void* stream);
 
 /* fp8probe_wall_clock_khz -- rate of the constant wall counter that
  * fp8probe_mfma records, in kHz, for the device `stream` runs on (NULL: the

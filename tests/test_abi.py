@@ -217,5 +217,8 @@ def test_probe_validation():
     assert lib.fp8probe_stream(GOOD, 64, GOOD, None, probe.SPLIT, None) == -1
     assert lib.fp8probe_stream(GOOD + 8, 64, GOOD, None, probe.COPY, None) == -5
     assert lib.fp8probe_stream(GOOD, 0, GOOD, None, probe.READ, None) == 0
+    assert lib.fp8probe_empty(0, 256, None) == -3
+    assert lib.fp8probe_empty(1, 0, None) == -3
+    assert lib.fp8probe_empty(1, 1025, None) == -3
     assert lib.fp8probe_mfma(0, 4, GOOD, GOOD, None) == -3
     assert lib.fp8probe_mfma(10, 4, None, GOOD, None) == -1

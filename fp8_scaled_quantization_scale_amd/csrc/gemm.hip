@@ -137,6 +137,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// 16 bytes of LDS at byte address addr (a constant added to addr lands in the
+// instruction's offset field)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_u4(uint32_t addr) {
+  const u32x4_t v = *(__attribute__((address_space(3))) const u32x4_t*)(size_t)addr;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  return *(__attribute__((address_space(3))) const float*)(size_t)addr;
+}
+
 // Wave-wide LDS DMA: LDS[m0 + 16 * lane] (dwordx4) or LDS[m0 + 4 * lane]
 // (dword) = buffer[voff + soff].  Inline asm so that the compiler's wait-count
 // pass does not treat it as an LDS store aliasing every later LDS read (which
@@ -203,6 +214,17 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
   const int wm = grp, wn = q;
   const int lr = lane & 15;  // fragment row
   const int lg = lane >> 4;  // lane group
+  // LDS byte offsets (within a stage) of the two 16-byte halves of the first
+  // fragment row this lane reads: A row wm kWM + lr, B row wn kWN + (lr / 4)
+  // CPL + lr % 4.  Its later rows (A: + 16 per sub-tile, B: + 4 per
+  // sub-tile, bits 0, 1 and 4 of the row unchanged) share that row's
+  // swizzle, so every fragment read is one of these plus a constant.
+  const int arow = wm * kWM + lr, brow0 = wn * kWN + (lr >> 2) * kCPL + (lr & 3);
+  const int swa = swz_a(arow), swb = swz_b(brow0);
+  const uint32_t fa_lo = (uint32_t)(arow * kBK + ((lg ^ swa) << 4));
+  const uint32_t fa_hi = (uint32_t)(arow * kBK + (((4 + lg) ^ swa) << 4));
+  const uint32_t fb_lo = (uint32_t)(kBM * kBK + brow0 * kBK + ((lg ^ swb) << 4));
+  const uint32_t fb_hi = (uint32_t)(kBM * kBK + brow0 * kBK + (((4 + lg) ^ swb) << 4));
 
 
   const int total = p.tiles_m * p.tiles_n;
@@ -350,9 +372,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
       for (int r = 0; r < 4; ++r) bsb[j][r] = 0.0f;
     int sax[S::kMx ? kMT : 1], sbx[S::kMx ? kNT : 1];  // E8M0 bytes of the lane's rows / columns
 
-    auto frag = [&](const uint8_t* base, int row, int sw) __attribute__((always_inline)) -> v8i {
-      const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kBK + ((lg ^ sw) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kBK + (((4 + lg) ^ sw) << 4));
+    // per-step LDS addresses of the lane's fragment rows (stage kt & 1) and
+    // of its A row scales, formed once per step in the load phase; every
+    // sub-tile's read then adds only a constant.  The empty asm keeps each a
+    // single register value, so the compiler does not re-form it per read.
+    uint32_t sa_lo = 0, sa_hi = 0, sb_lo = 0, sb_hi = 0, ssa = 0;
+    auto frag = [&](uint32_t lo_addr, uint32_t hi_addr) __attribute__((always_inline)) -> v8i {
+      const uint4 lo = lds_u4(lo_addr);
+      const uint4 hi = lds_u4(hi_addr);
       v8i f;
       f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
       f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
@@ -397,33 +424,37 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
       }
     };
 
-    // A sub-tile i of step kt (rows 16 i.. of the group's half) and its row scale
-    auto load_a = [&](int kt, int i) __attribute__((always_inline)) {  // i is a constant at every (inlined) call
-      const uint8_t* la = smem + (kt & 1) * kTileBytes;
-      const uint8_t* sc = &sscl[(kt / kSG) & 1][0];
-      const int row = wm * kWM + i * 16 + lr;
-      fa[i % kRingA] = frag(la, row, swz_a(row));
-      if constexpr (S::kRowA)
-        bsa[i % kRingS] = *reinterpret_cast<const float*>(sc + kSclALo + 16 * row + 4 * (kt % kSG));
+    // A sub-tile i of the step whose addresses the load phase set (rows 16 i..
+    // of the group's half) and its row scale
+    auto load_a = [&](int i) __attribute__((always_inline)) {  // i is a constant at every (inlined) call
+      fa[i % kRingA] = frag(sa_lo + (uint32_t)(i * 16 * kBK), sa_hi + (uint32_t)(i * 16 * kBK));
+      if constexpr (S::kRowA) bsa[i % kRingS] = lds_f32(ssa + (uint32_t)(16 * 16 * i));
     };
 
     // ---- load phase of step kt: B fragments and B-side scales into
     // registers, then the first A sub-tile of the group's own half
     auto load_phase = [&](int kt) __attribute__((always_inline)) {
-      const uint8_t* lb = smem + (kt & 1) * kTileBytes + kBM * kBK;
+      const uint32_t stage = lds_base + (uint32_t)((kt & 1) * kTileBytes);
+      sa_lo = fa_lo + stage;
+      sa_hi = fa_hi + stage;
+      sb_lo = fb_lo + stage;
+      sb_hi = fb_hi + stage;
+      if constexpr (S::kRowA)
+        ssa = scl_base + (uint32_t)(((kt / kSG) & 1) * kSclBytes + kSclALo + 16 * arow + 4 * (kt % kSG));
+      asm volatile("" : "+v"(sa_lo), "+v"(sa_hi), "+v"(sb_lo), "+v"(sb_hi));
+      if constexpr (S::kRowA) asm volatile("" : "+v"(ssa));
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        const int row = wn * kWN + brow(j);
-        fb[j] = frag(lb, row, swz_b(row));
-      }
+      for (int j = 0; j < kNT; ++j) fb[j] = frag(sb_lo + (uint32_t)(4 * j * kBK), sb_hi + (uint32_t)(4 * j * kBK));
       const uint8_t* sc = &sscl[(kt / kSG) & 1][0];
       const int ks = 4 * (kt % kSG);  // the step's word in a row's 16 bytes
       if constexpr (S::kRowB) {
+        uint32_t ssb = scl_base + (uint32_t)(((kt / kSG) & 1) * kSclBytes + kSclBLo + 16 * (wn * kWN + lg * kCPL) + ks);
+        asm volatile("" : "+v"(ssb));
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            bsb[j][e] = *reinterpret_cast<const float*>(sc + kSclBLo + 16 * (wn * kWN + lg * kCPL + 4 * j + e) + ks);
+            bsb[j][e] = lds_f32(ssb + (uint32_t)(16 * (4 * j + e)));
       }
       if constexpr (S::kTileB) stile = *reinterpret_cast<const float*>(sc + kSclBLo + 16 * (wn / 2) + ks);
       // this group's own A rows (landed by its own waits): the 2-D recipe's
@@ -436,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
         for (int i = 0; i < kMT; ++i) sax[i] = mx_byte(mx_at(sc, kSclALo, kSclAHi, wm * kWM + i * 16 + lr, b));
       }
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) load_a(kt, i);
+      for (int i = 0; i < kAhead; ++i) load_a(i);
       if constexpr (S::kMx) {
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
@@ -462,7 +493,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
       }
       static_for<kMT>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        if constexpr (i + kAhead < kMT) load_a(kt, i + kAhead);
+        if constexpr (i + kAhead < kMT) load_a(i + kAhead);
         static_for<kNT>([&](auto J) {
           constexpr int j = decltype(J)::value;
           constexpr int t = i * kNT + j;

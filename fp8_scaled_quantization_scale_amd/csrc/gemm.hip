@@ -147,6 +147,9 @@ __device__ __forceinline__ uint4 lds_u4(uint32_t addr) {
 __device__ __forceinline__ float lds_f32(uint32_t addr) {
   return *(__attribute__((address_space(3))) const float*)(size_t)addr;
 }
+__device__ __forceinline__ int lds_u8(uint32_t addr) {
+  return *(__attribute__((address_space(3))) const uint8_t*)(size_t)addr;
+}
 
 // Wave-wide LDS DMA: LDS[m0 + 16 * lane] (dwordx4) or LDS[m0 + 4 * lane]
 // (dword) = buffer[voff + soff].  Inline asm so that the compiler's wait-count
@@ -463,18 +466,25 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
       if constexpr (S::kTileA) stile *= *reinterpret_cast<const float*>(sc + kSclALo + 1024 * wm + ks);
       if constexpr (S::kMx) {
         const int b = mx_b(kt);
+        if (kt % kSG < kSG - 1) {
+          // b <= 14: every lane's byte is among its rows' 16 staged bytes,
+          // at a constant distance from its first row's
+          uint32_t xa = scl_base + (uint32_t)(((kt / kSG) & 1) * kSclBytes + kSclALo + 16 * arow + b);
+          uint32_t xb = scl_base + (uint32_t)(((kt / kSG) & 1) * kSclBytes + kSclBLo + 16 * brow0 + b);
+          asm volatile("" : "+v"(xa), "+v"(xb));
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) sax[i] = mx_byte(mx_at(sc, kSclALo, kSclAHi, wm * kWM + i * 16 + lr, b));
+          for (int i = 0; i < kMT; ++i) sax[i] = lds_u8(xa + (uint32_t)(16 * 16 * i));
+#pragma unroll
+          for (int j = 0; j < kNT; ++j) sbx[j] = lds_u8(xb + (uint32_t)(16 * 4 * j));
+        } else {
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) sax[i] = mx_byte(mx_at(sc, kSclALo, kSclAHi, wm * kWM + i * 16 + lr, b));
+#pragma unroll
+          for (int j = 0; j < kNT; ++j) sbx[j] = mx_byte(mx_at(sc, kSclBLo, kSclBHi, wn * kWN + brow(j), b));
+        }
       }
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) load_a(i);
-      if constexpr (S::kMx) {
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const int r = wn * kWN + brow(j);
-          sbx[j] = mx_byte(mx_at(sc, kSclBLo, kSclBHi, r, mx_b(kt)));
-        }
-      }
     };
 
     // ---- multiply phase of step kt: A fragments (and A row scales) stream

@@ -523,13 +523,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
         // barrier, holding every A fragment of the step live until then
         if constexpr (!S::kPromote)
           asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]), "+v"(acc[i][3]));
-        // issue order within the row: each MFMA followed by its share of the
-        // promotion arithmetic and one LDS read, so that the wave's in-order
-        // issue keeps the matrix pipe fed while the VALU work drains
+        // issue order within the row: each MFMA followed by up to 6 VALU
+        // instructions of the promotion arithmetic and one LDS read, so that
+        // the wave's in-order issue keeps the matrix pipe fed while the VALU
+        // work drains (a row carries about 15 of them with per-row A scales, 28
+        // with per-column B scales as well; groups of 6 timed best for both,
+        // ahead of 3-5 and 7-12)
         if constexpr (S::kPromote) {
           static_for<kNT>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, S::kRowB ? 12 : 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           });
         }

@@ -199,6 +199,9 @@ struct Scl {
   static constexpr bool kMx = REC == kGemmMx;
   static constexpr bool kPromote = kRowA || kTileA;
   static constexpr bool kSclAny = kRowA || kTileA || kRowB || kTileB || kMx;
+  // the wave's 12 DMA source offsets held in registers for the whole kernel
+  // (the per-column-scale and MX kernels have no room for them)
+  static constexpr bool kHoistDma = !kRowB && !kMx && REC != kGemmChannel;
 };
 
 template <int FA, int FB, int REC, int OUT>
@@ -279,19 +282,32 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     const uint32_t base_a = (uint32_t)((lane >> 3) * p.lda + chunk(true, 0));
     const uint32_t base_b0 = (uint32_t)((lane >> 3) * p.ldb + chunk(false, 0));
     const uint32_t base_b1 = (uint32_t)((lane >> 3) * p.ldb + chunk(false, 2));
+    // this wave's segments' offsets: A 16 grp + 4 q + i, B 32 + 8 q + i
+    uint32_t voa[S::kHoistDma ? 4 : 1], vob[S::kHoistDma ? 8 : 1];
+    if constexpr (S::kHoistDma) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) voa[i] = base_a + (uint32_t)(8 * (16 * grp + 4 * q + i)) * (uint32_t)p.lda;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vob[i] = ((i & 2) ? base_b1 : base_b0) + (uint32_t)(8 * (8 * q + i)) * (uint32_t)p.ldb;
+    }
     // (is_a is a constant at each call; the operand's resource and row stride
     // come in by value: a pick between the two variables would take their
     // addresses and keep them in private memory)
-    auto dma_tile = [&](int seg, int kt, bool is_a, __amdgpu_buffer_rsrc_t rs, int stride, auto Tail)
+    auto dma_tile = [&](int seg, int kt, bool is_a, __amdgpu_buffer_rsrc_t rs, int stride, auto Tail, int i)
         __attribute__((always_inline)) {
       const int k0 = kt * kBK;
       // the wave-uniform row offset 8 s ld (formed on the scalar unit; ld
       // passes through an empty asm so that it is formed at each use, not
       // hoisted per segment) joins the per-lane base in the range-checked
-      // vector offset
-      uint32_t ld = __builtin_amdgcn_readfirstlane((uint32_t)stride);
-      asm volatile("" : "+s"(ld));
-      uint32_t vo = (is_a ? base_a : ((seg & 2) ? base_b1 : base_b0)) + (uint32_t)(8 * (seg & 31)) * ld;
+      // vector offset -- or the offset comes from the registers set above
+      uint32_t vo;
+      if constexpr (S::kHoistDma) {
+        vo = is_a ? voa[i] : vob[i];
+      } else {
+        uint32_t ld = __builtin_amdgcn_readfirstlane((uint32_t)stride);
+        asm volatile("" : "+s"(ld));
+        vo = (is_a ? base_a : ((seg & 2) ? base_b1 : base_b0)) + (uint32_t)(8 * (seg & 31)) * ld;
+      }
       if constexpr (decltype(Tail)::value) {
         if (k0 + chunk(is_a, seg) >= p.K) vo = kOOB;
       }
@@ -335,13 +351,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     // go out with the first step of each group of kSG.
     auto issue_set = [&](int kt, auto Tail) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_tile(16 * grp + 4 * q + i, kt, true, ra, p.lda, Tail);
+      for (int i = 0; i < 4; ++i) dma_tile(16 * grp + 4 * q + i, kt, true, ra, p.lda, Tail, i);
       const bool scl = (kt % kSG) == 0;
       if constexpr (S::kRowA || S::kTileA || S::kMx)
         if (scl) dma_scl(kt, true, rsa);
       if (grp == 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dma_tile(32 + 8 * q + i, kt, false, rb, p.ldb, Tail);
+        for (int i = 0; i < 8; ++i) dma_tile(32 + 8 * q + i, kt, false, rb, p.ldb, Tail, i);
         if constexpr (S::kRowB || S::kTileB || S::kMx)
           if (scl) dma_scl(kt, false, rsb);
       }

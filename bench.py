@@ -39,6 +39,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -467,13 +468,18 @@ def _source_sha() -> str:
     """Hash of the sources that define the path's kernels and their launch
     configuration (the HIP files and the two internal headers; not the C
     ABI's host-side validation in api.cpp, which does not change what a
-    kernel moves, nor the measurement kernels of probe.hip)."""
+    kernel moves, nor the measurement kernels of probe.hip), comments and
+    blank space left out so that an edited comment does not orphan the
+    counters taken on the same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_scaled_quantization_scale_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if (f.endswith(".hip") and f != "probe.hip") or f in ("device.hpp", "launch.hpp"):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                text = fh.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # (no string literal in these holds // or /*)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

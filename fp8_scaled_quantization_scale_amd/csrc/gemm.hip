@@ -200,7 +200,7 @@ struct Scl {
   static constexpr bool kPromote = kRowA || kTileA;
   static constexpr bool kSclAny = kRowA || kTileA || kRowB || kTileB || kMx;
   // the wave's 12 DMA source offsets held in registers for the whole kernel
-  // (the per-column-scale and MX kernels have no room for them)
+  // (the channel, per-B-row-scale and MX kernels have no room for them)
   static constexpr bool kHoistDma = !kRowB && !kMx && REC != kGemmChannel;
 };
 
@@ -296,10 +296,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
     auto dma_tile = [&](int seg, int kt, bool is_a, __amdgpu_buffer_rsrc_t rs, int stride, auto Tail, int i)
         __attribute__((always_inline)) {
       const int k0 = kt * kBK;
-      // the wave-uniform row offset 8 s ld (formed on the scalar unit; ld
-      // passes through an empty asm so that it is formed at each use, not
-      // hoisted per segment) joins the per-lane base in the range-checked
-      // vector offset -- or the offset comes from the registers set above
+      // the segment's offset: from the registers set above, or the lane's
+      // base plus the wave-uniform row offset 8 s ld (formed on the scalar
+      // unit; ld passes through an empty asm so that it is formed at each
+      // use, not hoisted per segment).  Either way the row part sits in the
+      // range-checked vector offset, so rows past the matrix read as zero.
       uint32_t vo;
       if constexpr (S::kHoistDma) {
         vo = is_a ? voa[i] : vob[i];

@@ -186,7 +186,6 @@ template <typename InT>
 struct Raw;
 template <>
 struct Raw<uint16_t> {
-  static constexpr int kWords = 8;
   uint4 w[8];
   __device__ __forceinline__ void row(int i, float v[8]) const { unpack_bf16x8(w[i], v); }
   __device__ __forceinline__ uint32_t key(int i, const float*) const { return bf16x8_key(w[i]); }
@@ -208,7 +207,6 @@ struct Raw<uint16_t> {
 };
 template <>
 struct Raw<float> {
-  static constexpr int kWords = 16;
   float4 w[16];
   __device__ __forceinline__ uint32_t key(int, const float* v) const { return max8_key(v); }
   __device__ __forceinline__ void row(int i, float v[8]) const {

@@ -18,9 +18,11 @@ so quantization time counts against it.
     the timed steps with HIP events on the stream it runs on, in every E-th
     step (--event-every); "roofline_fprop" the same for the fprop GEMM, the
     blockwise kernel the method's throughput target names.  Each carries the
-    fraction of the 5.0 PFLOP/s datasheet peak and of the rate the matrix
+    fraction of the 5.0 PFLOP/s datasheet peak and of the rates the matrix
     cores sustain on this GPU under full FP8 load ("mfma_ceiling", measured
-    by libfp8mi_probe.so together with the shader clock under that load).
+    by libfp8mi_probe.so together with the shader clock under that load):
+    with fixed operands (the clock limit) and with operands that change
+    from product to product as a GEMM's do ("varied", the power limit).
   * "kernels": each op alone over back-to-back launches; casts report GB/s
     against the 8 TB/s datasheet figure and against "hbm_ceiling", in-tree
     streaming kernels at the cast's own read:write byte mix.
@@ -531,15 +533,12 @@ def hbm_ceilings(ev: "HipEvents") -> dict:
     return {"gbs": out, "hints": hints}
 
 
-def mfma_ceiling(ev: "HipEvents") -> dict:
-    """FP8 matrix-core rate this GPU sustains under full load (registers only,
-    two waves per SIMD, one workgroup per compute unit), and the shader clock
-    during it from the core and wall cycle counters of every workgroup."""
+def _mfma_rate(ev: "HipEvents", varied: bool) -> dict:
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     iters = 60000
     clocks = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    ms = _time_ms(lambda: probe.mfma(iters, cus, clocks, sink), 1, ev)
+    ms = _time_ms(lambda: probe.mfma(iters, cus, clocks, sink, varied), 1, ev)
     flops = cus * probe.MFMA_WAVES * iters * probe.MFMA_FLOPS_PER_ROUND
     c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
     wall_khz = probe.wall_clock_khz()
@@ -547,9 +546,22 @@ def mfma_ceiling(ev: "HipEvents") -> dict:
     tf = flops / (ms * 1e-3) / 1e12
     return {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3), "cus": cus,
             "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4),
-            "peak_at_clock_tflops": round(PEAK_FP8_TFLOPS * ghz / PEAK_CLOCK_GHZ, 1),
-            "note": "back-to-back 16x16x128 FP8 MFMAs from registers on every SIMD; clock = core cycles / "
-                    "wall cycles x the wall counter's rate, median over workgroups"}
+            "peak_at_clock_tflops": round(PEAK_FP8_TFLOPS * ghz / PEAK_CLOCK_GHZ, 1)}
+
+
+def mfma_ceiling(ev: "HipEvents") -> dict:
+    """FP8 matrix-core rate this GPU sustains under full load (registers only,
+    two waves per SIMD, one workgroup per compute unit), and the shader clock
+    during it from the core and wall cycle counters of every workgroup: with
+    fixed operands (top level: the clock limit) and with operands that change
+    from product to product ("varied": the multipliers switch as in a GEMM
+    over real data, which costs power and clock)."""
+    out = _mfma_rate(ev, False)
+    out["varied"] = _mfma_rate(ev, True)
+    out["note"] = ("back-to-back 16x16x128 FP8 MFMAs from registers on every SIMD; clock = core cycles / wall "
+                   "cycles x the wall counter's rate, median over workgroups; varied: four operand sets per "
+                   "lane cycled so that each product multiplies other codes")
+    return out
 
 
 def calibrate_copy(nbytes: int):
@@ -701,6 +713,7 @@ def _roofline(name: str, flops: int, launch_ms, ceiling: dict, workload: str) ->
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
             "frac_of_mfma_ceiling": round(achieved / ceiling["tflops"], 4),
             "frac_at_probe_clock": round(achieved / ceiling["peak_at_clock_tflops"], 4),
+            "frac_of_mfma_ceiling_varied": round(achieved / ceiling["varied"]["tflops"], 4),
             "traffic": _traffic(workload, name), "launches_timed": len(launch_ms),
             "launch_ms_mean": round(ms, 4), "flops_per_launch": flops}
 
@@ -807,7 +820,9 @@ def main():
         empty.append(ev.ms(0) * 1e3)
 
     ceil_hbm = hbm_ceilings(ev) if not args.no_probes else None
-    ceil_mfma = mfma_ceiling(ev) if not args.no_probes else {"tflops": float("nan"), "peak_at_clock_tflops": float("nan")}
+    nan = float("nan")
+    ceil_mfma = mfma_ceiling(ev) if not args.no_probes else {"tflops": nan, "peak_at_clock_tflops": nan,
+                                                             "varied": {"tflops": nan}}
 
     kernels = {}
     for (name, kind, work, _), ms in zip(step.ops, op_ms):

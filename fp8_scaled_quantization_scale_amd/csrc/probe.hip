@@ -1,5 +1,6 @@
 // probe.hip -- measurement kernels behind include/fp8mi_probe.h: the matrix
-// cores' rate and the shader clock under full FP8 MFMA load, and plain HBM
+// cores' rate and the shader clock under full FP8 MFMA load (fixed or varied
+// operands), and plain HBM
 // streams at the quantize kernels' read:write mixes.  They bound what the
 // FP8 path can reach on this GPU; they are not part of the method.
 #include <hip/hip_runtime.h>
@@ -109,15 +110,40 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const uint4* __r
   }
 }
 
+// Per-lane hash (a 32-bit integer mixer) for the varied operands.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+// SETS == 1: every product multiplies the same codes (E4M3 1.0 and 0.5,
+// perturbed per lane), so the multipliers barely switch and the clock is
+// the chip's limit.  SETS == 4: four operand sets per lane from the hash
+// (E4M3 codes with the lowest exponent bit cleared, which excludes the NaN
+// pattern), cycled so that each product multiplies other codes than the one
+// before it, as in a GEMM.
+template <int SETS>
 __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(int iters, uint64_t* clocks, float* sink) {
   __shared__ float pad[kMfmaLdsWords];  // holds the compute unit: one workgroup each
-  v8i a, b;  // E4M3 codes of 1.0 and 0.5, perturbed per lane
+  v8i a[SETS], b[SETS];
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = 0x38383838 ^ (t & 7);
-    b[i] = 0x30303030 ^ ((t >> 3) & 7);
-  }
+  for (int s = 0; s < SETS; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (SETS == 1) {
+        a[s][i] = 0x38383838 ^ (t & 7);
+        b[s][i] = 0x30303030 ^ ((t >> 3) & 7);
+      } else {
+        const uint32_t h = ((blockIdx.x * 64u * kMfmaWaves + (uint32_t)t) * SETS + (uint32_t)s) * 8u + (uint32_t)i;
+        a[s][i] = (int)(mix32(h) & 0xF7F7F7F7u);
+        b[s][i] = (int)(mix32(h ^ 0x9E3779B9u) & 0xF7F7F7F7u);
+      }
+    }
   v4f acc[kMfmaAcc];
 #pragma unroll
   for (int j = 0; j < kMfmaAcc; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -126,7 +152,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_kernel(int iters, uint64
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < kMfmaAcc; ++j)
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[j], 0, 0, 0, 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[j % SETS], b[(j + j / SETS) % SETS], acc[j], 0, 0, 0,
+                                                                 0, 0, 0);
   }
   __syncthreads();
   const uint64_t c1 = (uint64_t)clock64(), w1 = (uint64_t)wall_clock64();
@@ -206,7 +233,14 @@ int fp8probe_stream(const void* src, int64_t n16, void* dst0, void* dst1, int mi
 int fp8probe_mfma(int iters, int workgroups, uint64_t* clocks, float* sink, void* stream) {
   if (iters < 1 || workgroups < 1) return -3;
   if (!clocks || !sink) return -1;
-  mfma_kernel<<<(unsigned)workgroups, 64 * kMfmaWaves, 0, (hipStream_t)stream>>>(iters, clocks, sink);
+  mfma_kernel<1><<<(unsigned)workgroups, 64 * kMfmaWaves, 0, (hipStream_t)stream>>>(iters, clocks, sink);
+  return launched();
+}
+
+int fp8probe_mfma_varied(int iters, int workgroups, uint64_t* clocks, float* sink, void* stream) {
+  if (iters < 1 || workgroups < 1) return -3;
+  if (!clocks || !sink) return -1;
+  mfma_kernel<4><<<(unsigned)workgroups, 64 * kMfmaWaves, 0, (hipStream_t)stream>>>(iters, clocks, sink);
   return launched();
 }
 

@@ -1,6 +1,7 @@
 """Binding of libfp8mi_probe.so (include/fp8mi_probe.h): the measurement
 kernels bench.py uses to state what this GPU sustains -- the FP8 matrix-core
-rate and shader clock under full load, HBM streams at the quantize
+rate and shader clock under full load (fixed and varied operands), HBM
+streams at the quantize
 kernels' read:write mixes, and the cost of an empty launch.  Argument
 marshalling only."""
 from __future__ import annotations
@@ -15,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8mi_probe.so")
 
 READ, COPY, HALF, SPLIT = 0, 1, 2, 3
 NT_LOAD, NT_STORE, BLOCKED = 16, 32, 64  # access hints, OR-ed into a mix
-EXPORTS = ("fp8probe_stream", "fp8probe_mfma", "fp8probe_empty", "fp8probe_wall_clock_khz")
+EXPORTS = ("fp8probe_stream", "fp8probe_mfma", "fp8probe_mfma_varied", "fp8probe_empty", "fp8probe_wall_clock_khz")
 MFMA_WAVES = 8                  # waves per workgroup of fp8probe_mfma
 MFMA_FLOPS_PER_ROUND = 8 * 2 * 16 * 16 * 128  # eight 16x16x128 products per wave per round
 
@@ -34,6 +35,8 @@ def load(path: str = LIB_PATH):
     lib.fp8probe_stream.argtypes = [vp, i64, vp, vp, i32, vp]
     lib.fp8probe_mfma.restype = i32
     lib.fp8probe_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.fp8probe_mfma_varied.restype = i32
+    lib.fp8probe_mfma_varied.argtypes = [i32, i32, vp, vp, vp]
     lib.fp8probe_empty.restype = i32
     lib.fp8probe_empty.argtypes = [i32, i32, vp]
     lib.fp8probe_wall_clock_khz.restype = i32
@@ -64,13 +67,19 @@ def stream(src: torch.Tensor, dst0: torch.Tensor, dst1: torch.Tensor | None, mix
         raise RuntimeError(f"fp8probe_stream failed ({st})")
 
 
-def mfma(iters: int, workgroups: int, clocks: torch.Tensor, sink: torch.Tensor) -> None:
-    """One launch of fp8probe_mfma; clocks: int64 [4 * workgroups], sink: float32 [1]."""
+def mfma(iters: int, workgroups: int, clocks: torch.Tensor, sink: torch.Tensor, varied: bool = False) -> None:
+    """One launch of fp8probe_mfma (fixed operands) or, with varied=True,
+    fp8probe_mfma_varied (operands that change from product to product);
+    clocks: int64 [4 * workgroups], sink: float32 [1], both on the device."""
+    for t in (clocks, sink):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise RuntimeError("probe buffers must be contiguous device tensors")
     if clocks.numel() < 4 * workgroups or clocks.dtype != torch.int64 or sink.dtype != torch.float32:
         raise RuntimeError("clocks must be int64 [4 * workgroups], sink float32")
-    st = load().fp8probe_mfma(iters, workgroups, clocks.data_ptr(), sink.data_ptr(), _stream())
+    fn = load().fp8probe_mfma_varied if varied else load().fp8probe_mfma
+    st = fn(iters, workgroups, clocks.data_ptr(), sink.data_ptr(), _stream())
     if st != 0:
-        raise RuntimeError(f"fp8probe_mfma failed ({st})")
+        raise RuntimeError(f"fp8probe_mfma{'_varied' if varied else ''} failed ({st})")
 
 
 def empty(workgroups: int = 1, threads: int = 256) -> None:

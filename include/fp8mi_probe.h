@@ -7,7 +7,8 @@
  * Why: "From FP16 to FP8", sec. 3.1 judges an FP8 GEMM benchmark by the
  * fraction of the theoretical rate it reaches.  The datasheet peaks assume
  * the top clock and ideal memory; these kernels measure the matrix-core
- * rate and shader clock under full FP8 MFMA load, and the HBM rate of plain
+ * rate and shader clock under full FP8 MFMA load (with fixed and with
+ * varied operands), and the HBM rate of plain
  * streams with the quantize kernels' read:write byte mixes, and the cost
  * of an empty launch.
  *
@@ -62,6 +63,17 @@ int fp8probe_stream(const void* src, int64_t n16, void* dst0, void* dst1, int mi
  * written in practice (keeps the products live).
  * Returns FP8MI_OK, -1 (NULL pointer), -3 (iters or workgroups < 1) or -6. */
 int fp8probe_mfma(int iters, int workgroups, uint64_t* clocks, float* sink, void* stream);
+
+/* fp8probe_mfma_varied -- fp8probe_mfma with operands that change from one
+ * product to the next: each lane holds four sets of E4M3 codes drawn from
+ * a hash of its position (the lowest exponent bit cleared, so no code is
+ * NaN) and the eight products of a round cycle through them, so that the
+ * multipliers switch as they do in a GEMM over real data.  Switching costs
+ * power, so this load runs at a lower clock than fp8probe_mfma's fixed
+ * operands: its rate is the matrix-core ceiling a GEMM over real data can
+ * approach, fp8probe_mfma's the chip's clock limit.  Same arguments, flops,
+ * clocks layout and return values as fp8probe_mfma. */
+int fp8probe_mfma_varied(int iters, int workgroups, uint64_t* clocks, float* sink, void* stream);
 
 /* fp8probe_empty -- one launch of a kernel with an empty body, `workgroups`
  * workgroups of `threads` threads: the cost of a dispatch alone, the floor

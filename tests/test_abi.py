@@ -222,3 +222,6 @@ def test_probe_validation():
     assert lib.fp8probe_empty(1, 1025, None) == -3
     assert lib.fp8probe_mfma(0, 4, GOOD, GOOD, None) == -3
     assert lib.fp8probe_mfma(10, 4, None, GOOD, None) == -1
+    assert lib.fp8probe_mfma_varied(0, 4, GOOD, GOOD, None) == -3
+    assert lib.fp8probe_mfma_varied(10, 0, GOOD, GOOD, None) == -3
+    assert lib.fp8probe_mfma_varied(10, 4, GOOD, None, None) == -1

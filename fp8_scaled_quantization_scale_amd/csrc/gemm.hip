@@ -200,8 +200,9 @@ struct Scl {
   static constexpr bool kPromote = kRowA || kTileA;
   static constexpr bool kSclAny = kRowA || kTileA || kRowB || kTileB || kMx;
   // the wave's 12 DMA source offsets held in registers for the whole kernel
-  // (the channel, per-B-row-scale and MX kernels have no room for them)
-  static constexpr bool kHoistDma = !kRowB && !kMx && REC != kGemmChannel;
+  // (the channel, per-B-row-scale, MX and 1x128 x 128x128 kernels have no
+  // room for them)
+  static constexpr bool kHoistDma = !kRowB && !kMx && REC != kGemmChannel && REC != kGemmBlock128x128;
 };
 
 template <int FA, int FB, int REC, int OUT>
@@ -527,6 +528,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
           if constexpr (S::kPromote) {
             part[t % (kLag + 1)] = mfma<FB, FA>(fb[j], fa[i % kRingA], v4f{0.0f, 0.0f, 0.0f, 0.0f});
             if constexpr (t >= kLag) promote(std::integral_constant<int, t - kLag>{});
+            // one scale per product (an A row or tile scale times the B tile
+            // scale): each MFMA followed by exactly the four promotion FMAs
+            // of the product kLag before it.  The wave's in-order issue hides
+            // an even four per 16x16x128 product far better than the uneven
+            // groups the scheduler forms by itself
+            if constexpr (!S::kRowB) __builtin_amdgcn_sched_barrier(0);
           } else if constexpr (S::kMx) {
             acc[i][j] = mfma_mx<FB, FA>(fb[j], fa[i % kRingA], acc[i][j], sbx[j], sax[i]);
           } else if constexpr (REC == kGemmBf16) {
@@ -540,13 +547,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
         // barrier, holding every A fragment of the step live until then
         if constexpr (!S::kPromote)
           asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]), "+v"(acc[i][3]));
-        // issue order within the row: each MFMA followed by up to 6 VALU
-        // instructions of the promotion arithmetic and one LDS read, so that
-        // the wave's in-order issue keeps the matrix pipe fed while the VALU
-        // work drains (a row carries about 15 of them with per-row A scales, 28
-        // with per-column B scales as well; groups of 6 timed best for both,
-        // ahead of 3-5 and 7-12)
-        if constexpr (S::kPromote) {
+        // per-column B scales as well (a scale product and an FMA per
+        // element): each MFMA followed by up to 6 VALU instructions of the
+        // promotion arithmetic and one LDS read, so that the wave's in-order
+        // issue keeps the matrix pipe fed while the VALU work drains (a row
+        // carries about 28 of them; groups of 6 timed best, ahead of 3-5,
+        // 7-12 and a strict eight after each MFMA)
+        if constexpr (S::kPromote && S::kRowB) {
           static_for<kNT>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);

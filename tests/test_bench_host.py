@@ -45,3 +45,12 @@ def test_traffic_entry_needs_the_current_hash(tmp_path, monkeypatch):
     assert bench._traffic("w", "gemm_fprop") == 123
     assert bench._traffic("w", "gemm_dgrad") is None
     assert bench._traffic("other", "gemm_fprop") is None
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr

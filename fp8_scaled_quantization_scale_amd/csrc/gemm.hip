@@ -551,8 +551,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GArgs p) {
         // element): each MFMA followed by up to 6 VALU instructions of the
         // promotion arithmetic and one LDS read, so that the wave's in-order
         // issue keeps the matrix pipe fed while the VALU work drains (a row
-        // carries about 28 of them; groups of 6 timed best, ahead of 3-5,
-        // 7-12 and a strict eight after each MFMA)
+        // carries 32 of them; groups of 6 timed best, ahead of 3-5, 7-12
+        // and a strict eight after each MFMA)
         if constexpr (S::kPromote && S::kRowB) {
           static_for<kNT>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
